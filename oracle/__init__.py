@@ -1,0 +1,15 @@
+"""fp64 CPU oracle of the Kara window-compression step (test infrastructure only).
+
+Only the test suite, the package smoke check and the benchmark's cpu_baseline
+leg may import this package; the product path never does.
+"""
+from .kara_oracle import (  # noqa: F401
+    Selection,
+    compact_paged_sequence,
+    compact_window_rows,
+    compress_step,
+    gather_window_rows,
+    rewrite_block_table,
+    token2chunk_select,
+    window_scores,
+)

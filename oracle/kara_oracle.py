@@ -1,0 +1,276 @@
+"""Plain fp64 CPU oracle of Kara's decode-time window-compression step.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only the test suite, the package smoke check and the
+benchmark's ``cpu_baseline`` leg use it.  It shares no code, table or constant
+with the HIP path and imports nothing from the package.
+
+Sources (cited by page title and section; the pages give no equations):
+
+* [Kara-abs]  "Kara: Efficient Reasoning LLM Serving via Sliding-Window KV
+  Cache Compression", the authors' English abstract (shd-paper.top, section
+  "摘要（原文）"; repeated on fugumt.com).  It fixes: compression runs at decode
+  time on the most recently generated context only; KV pairs in that window
+  are scored and selected with *bidirectional* attention; a Token2Chunk module
+  grows a subset of the selected pairs into chunks; the result lives in a
+  PagedAttention cache whose memory shrinks.
+* [Kara-method]  same page, section "方法详解": the window module selects KV
+  pairs while decoding, Token2Chunk turns selected pairs into chunks
+  dynamically, and the design is adapted to PagedAttention.
+* [gist-de]  gist.science/de explainer of the same paper (AI-written, not by
+  the authors), sections "1. Die Zwei-Wege-Konversations-Bewertung" and
+  "2. Das Token2Chunk-Modul": the score is a two-way attention measure
+  inside the sliding window; chunks have no fixed size.
+
+Readings taken where the pages are silent (each is stated where used):
+
+* R1/R2  score of window key j = sum over the G query heads of the KV group
+  and over all W window queries of softmax(q k^T / sqrt(d)) mass on column j;
+  the softmax spans the W window keys only, unmasked (both directions),
+  diagonal included.
+* R3/R4  queries are the window's own query vectors as stored; query head h
+  belongs to KV head floor(h / G).
+* R9-R13 Token2Chunk rule: seeds = the first ``seeds`` positions of the order
+  (score desc, position asc); every seed grows to the span
+  [p - radius, p + radius] clipped to the window; spans are merged; the rest
+  of the budget goes to the best positions outside the spans, by the same
+  order; exactly ``budget`` positions are kept, listed in ascending order.
+* R14-R18 compaction is in place: logical slot L + r receives the row that
+  sat in slot L + kept[r]; block-table entries past the new length are freed
+  in ascending logical order and set to -1; every other byte is unchanged.
+
+Parity pins for each function live in ``tests/test_oracle_*.py``.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+__all__ = [
+    "window_scores",
+    "Selection",
+    "token2chunk_select",
+    "gather_window_rows",
+    "compact_window_rows",
+    "compact_paged_sequence",
+    "rewrite_block_table",
+    "compress_step",
+]
+
+
+# --------------------------------------------------------------------------
+# a2-a4: bidirectional in-window attention scores  [Kara-abs], [gist-de §1]
+# --------------------------------------------------------------------------
+def window_scores(q_group, k_window):
+    """Column mass of bidirectional in-window attention for one unit.
+
+    Parameters
+    ----------
+    q_group : array [G, W, d]
+        The window's query vectors of the G query heads that share one KV head.
+    k_window : array [W, d]
+        The window's key vectors of that KV head, in logical order.
+
+    Returns
+    -------
+    c : float64 array [W]
+        c[j] = sum_h sum_i softmax_j'(q[h,i] . k[j'] / sqrt(d))[j]   (R1, R2).
+
+    Every value is upcast exactly to fp64; the softmax is taken per query row
+    over all W window keys with no causal mask.  The row maximum is subtracted
+    before exponentiation (this leaves the value unchanged and keeps exp in
+    range).
+    """
+    q = np.asarray(q_group, dtype=np.float64)
+    k = np.asarray(k_window, dtype=np.float64)
+    if q.ndim != 3 or k.ndim != 2 or q.shape[1] != k.shape[0] or q.shape[2] != k.shape[1]:
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape}")
+    G, W, d = q.shape
+    c = np.zeros(W, dtype=np.float64)
+    if W == 0:
+        return c
+    inv_sqrt_d = 1.0 / math.sqrt(d)
+    for h in range(G):
+        logits = (q[h] @ k.T) * inv_sqrt_d          # [W queries, W keys]
+        row_max = logits.max(axis=1, keepdims=True)
+        weights = np.exp(logits - row_max)
+        probs = weights / weights.sum(axis=1, keepdims=True)
+        c += probs.sum(axis=0)                      # column mass
+    return c
+
+
+# --------------------------------------------------------------------------
+# a5-a8: Token2Chunk selection  [Kara-abs], [Kara-method]; rule R9-R13
+# --------------------------------------------------------------------------
+@dataclass
+class Selection:
+    kept: np.ndarray        # int64 [budget], ascending window-relative positions
+    seeds: np.ndarray       # int64 [seeds], in selection order (best first)
+    span: np.ndarray        # bool [W], union of the clipped seed spans (U)
+    fill: np.ndarray        # int64, singletons added outside U, best first (F)
+
+
+def _order(scores):
+    """Positions sorted by the total order (score descending, position ascending)."""
+    vals = [float(x) for x in scores]
+    return sorted(range(len(vals)), key=lambda j: (-vals[j], j))
+
+
+def token2chunk_select(scores, budget, seeds, radius):
+    """Select exactly ``budget`` window positions (R9-R13).
+
+    1. seeds  = first ``seeds`` positions of the order (score desc, pos asc);
+    2. U      = union over seeds p of [max(0, p - radius), min(W - 1, p + radius)];
+    3. F      = first (budget - |U|) positions of the same order not in U;
+    4. kept   = U and F together, ascending.
+    Requires 0 <= seeds, 0 <= radius, seeds * (2 * radius + 1) <= budget <= W.
+    """
+    W = len(scores)
+    if not (0 <= seeds and 0 <= radius and seeds * (2 * radius + 1) <= budget <= W):
+        raise ValueError("need seeds*(2*radius+1) <= budget <= W")
+    order = _order(scores)
+    seed_pos = order[:seeds]
+    span = np.zeros(W, dtype=bool)
+    for p in seed_pos:
+        lo = max(0, p - radius)
+        hi = min(W - 1, p + radius)
+        span[lo:hi + 1] = True
+    room = budget - int(span.sum())
+    fill = [j for j in order if not span[j]][:room]
+    keep = span.copy()
+    keep[fill] = True
+    kept = np.flatnonzero(keep).astype(np.int64)
+    assert kept.size == budget
+    return Selection(kept=kept, seeds=np.asarray(seed_pos, dtype=np.int64),
+                     span=span, fill=np.asarray(fill, dtype=np.int64))
+
+
+# --------------------------------------------------------------------------
+# a1: window addressing through a PagedAttention block table  [Kara-abs]
+# --------------------------------------------------------------------------
+def _slot(table_row, pos, block_size):
+    blk = int(table_row[pos // block_size])
+    if blk < 0:
+        raise IndexError(f"logical position {pos} maps to an unassigned block")
+    return blk, pos % block_size
+
+
+def gather_window_rows(pool, table_row, layer, kv_head, start, count, block_size):
+    """Rows of logical slots [start, start+count) of one (layer, kv head).
+
+    ``pool`` is [layers][num_blocks][kv_heads][block_size][d]; a logical slot p
+    lives in physical block table_row[p // block_size] at offset p % block_size.
+    """
+    out = []
+    for p in range(start, start + count):
+        blk, off = _slot(table_row, p, block_size)
+        out.append(np.array(pool[layer, blk, kv_head, off], copy=True))
+    if not out:
+        return np.zeros((0,) + pool.shape[4:], dtype=pool.dtype)
+    return np.stack(out)
+
+
+# --------------------------------------------------------------------------
+# a9: compaction  (R14, R15)
+# --------------------------------------------------------------------------
+def compact_window_rows(rows, kept):
+    """Dense form of the in-place compaction of one unit's window.
+
+    ``rows`` is [W, ...].  Returns a copy in which row r (r < len(kept)) holds
+    the old row kept[r]; rows at and past len(kept) keep their old contents.
+    """
+    out = np.array(rows, copy=True)
+    src = np.array(rows, copy=True)
+    for r, j in enumerate(kept):
+        out[r] = src[int(j)]
+    return out
+
+
+def compact_paged_sequence(k_pool, v_pool, table_row, prior_len, kept, block_size):
+    """Apply the compaction of every (layer, kv head) of one sequence, in place.
+
+    ``kept`` is [layers][kv_heads][B].  For each (layer, head) and r < B, the
+    K and V rows of logical slot prior_len + r become the old rows of slot
+    prior_len + kept[r]; all old rows are read before any is written.
+    """
+    layers, kv_heads, B = kept.shape
+    for pool in (k_pool, v_pool):
+        for layer in range(layers):
+            for g in range(kv_heads):
+                old = []
+                for j in kept[layer, g]:
+                    blk, off = _slot(table_row, prior_len + int(j), block_size)
+                    old.append(pool[layer, blk, g, off].copy())
+                for r in range(B):
+                    blk, off = _slot(table_row, prior_len + r, block_size)
+                    pool[layer, blk, g, off] = old[r]
+
+
+# --------------------------------------------------------------------------
+# a10: block-table rewrite and freed list  (R16, R17)
+# --------------------------------------------------------------------------
+def rewrite_block_table(table_row, prior_len, window, budget, block_size):
+    """Truncate one sequence's block table after compaction.
+
+    Blocks holding logical slots < prior_len + budget stay; the entries of
+    logical blocks ceil((L+B)/bs) .. ceil((L+W)/bs)-1 are returned in that
+    order as freed and replaced by -1.  Returns (new_row, freed, new_len).
+    """
+    row = np.array(table_row, copy=True)
+    nb_old = -(-(prior_len + window) // block_size)
+    nb_new = -(-(prior_len + budget) // block_size)
+    freed = row[nb_new:nb_old].copy()
+    row[nb_new:nb_old] = -1
+    return row, freed, prior_len + budget
+
+
+# --------------------------------------------------------------------------
+# The whole step over a batch
+# --------------------------------------------------------------------------
+def compress_step(q, k_pool, v_pool, block_tables, prior_lens, *, window, budget,
+                  seeds, radius, block_size, scores_override=None):
+    """Run a1-a10 for every sequence, layer and KV head.
+
+    q            [S][layers][W][Hq][d]
+    k_pool/v_pool [layers][num_blocks][Hkv][block_size][d]   (copied, not modified)
+    block_tables [S][max_blocks] int
+    prior_lens   [S] int
+    scores_override  optional [S][layers][Hkv][W]: select from these scores
+                 instead of the oracle's own (used to pin the selection and
+                 compaction stages to scores computed elsewhere).
+    Returns a dict with scores, kept, k_pool, v_pool, block_tables, seq_lens,
+    freed (list of arrays) and num_freed.
+    """
+    S, layers, W, Hq, d = q.shape
+    Hkv = k_pool.shape[2]
+    G = Hq // Hkv
+    assert W == window
+    k_out = np.array(k_pool, copy=True)
+    v_out = np.array(v_pool, copy=True)
+    tables = np.array(block_tables, copy=True)
+    scores = np.zeros((S, layers, Hkv, W), dtype=np.float64)
+    kept = np.zeros((S, layers, Hkv, budget), dtype=np.int64)
+    seq_lens = np.zeros(S, dtype=np.int64)
+    freed, num_freed = [], np.zeros(S, dtype=np.int64)
+    for n in range(S):
+        L = int(prior_lens[n])
+        for layer in range(layers):
+            for g in range(Hkv):
+                if scores_override is None:
+                    qg = np.transpose(q[n, layer, :, g * G:(g + 1) * G, :], (1, 0, 2))
+                    kw = gather_window_rows(k_pool, block_tables[n], layer, g, L, W, block_size)
+                    scores[n, layer, g] = window_scores(qg, kw)
+                else:
+                    scores[n, layer, g] = np.asarray(scores_override[n, layer, g], dtype=np.float64)
+                kept[n, layer, g] = token2chunk_select(scores[n, layer, g], budget, seeds, radius).kept
+        compact_paged_sequence(k_out, v_out, block_tables[n], L, kept[n], block_size)
+        row, fr, new_len = rewrite_block_table(block_tables[n], L, W, budget, block_size)
+        tables[n] = row
+        freed.append(fr)
+        num_freed[n] = fr.size
+        seq_lens[n] = new_len
+    return dict(scores=scores, kept=kept, k_pool=k_out, v_pool=v_out, block_tables=tables,
+                seq_lens=seq_lens, freed=freed, num_freed=num_freed)
