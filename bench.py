@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""Benchmark of the Kara window-compression step on one MI355X.
+
+One step = kara_score_window + kara_select_chunks + kara_compact_paged over
+every (sequence, layer, KV head) of the workload, inputs resident in HBM.
+Between steps the window blocks and block tables are restored from a
+pristine copy (outside the timed events; compaction is in place).
+
+Prints ONE JSON line: metric, value (window tokens per second), per-stage
+times, the roofline of the dominant kernel, and the fp64 CPU oracle timed on
+a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "window tokens compressed/sec (score+select+compact), 8B shape; % of roofline"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="llama8b_b64")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the oracle sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "decode_kv_cache_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel_hash):
+    """HBM bytes per launch of the scoring call from committed PMC runs, if the
+    kernels have not changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(workload)
+    if not rec or rec.get("kernel_hash") != kernel_hash:
+        return None
+    return rec.get("score_bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------- CPU oracle baseline
+def _oracle_unit(args):
+    import numpy as np
+    import oracle
+    qg, kw, krows, vrows, B, s, r = args
+    t0 = time.perf_counter()
+    c = oracle.window_scores(qg, kw)
+    sel = oracle.token2chunk_select(c, B, s, r)
+    oracle.compact_window_rows(krows, sel.kept)
+    oracle.compact_window_rows(vrows, sel.kept)
+    return time.perf_counter() - t0
+
+
+def _pool_init():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+
+
+def cpu_baseline(wl, shape, target_s):
+    """Time the oracle (score + select + compact per unit) on a seeded sample."""
+    import multiprocessing as mp
+
+    import numpy as np
+    import torch
+    procs = max(1, min(16, os.cpu_count() or 1))
+    rng = np.random.default_rng(1234)
+    G, W, bs = shape.group, shape.window, shape.block_size
+
+    def unit_args(u):
+        n, rest = divmod(int(u), shape.num_layers * shape.num_kv_heads)
+        layer, g = divmod(rest, shape.num_kv_heads)
+        L = int(wl.host_prior_lens[n])
+        pos = np.arange(L, L + W)
+        blk = torch.from_numpy(wl.host_tables[n, pos // bs].astype(np.int64)).to(wl.k_pool.device)
+        off = torch.from_numpy((pos % bs).astype(np.int64)).to(wl.k_pool.device)
+        kr = wl.k_pool[layer][blk, g, off, :]
+        vr = wl.v_pool[layer][blk, g, off, :]
+        qg = wl.q[n, layer, :, g * G:(g + 1) * G, :].permute(1, 0, 2)
+        bits = torch.int16 if kr.dtype == torch.bfloat16 else torch.int32
+        return (qg.double().cpu().numpy(), kr.double().cpu().numpy(), kr.view(bits).cpu().numpy(),
+                vr.view(bits).cpu().numpy(), shape.budget, shape.seeds, shape.radius)
+
+    units = shape.units
+    t1 = _oracle_unit(unit_args(0))                    # calibration (single unit, this process)
+    n = int(max(procs, min(units, round(target_s * procs / max(t1, 1e-6)))))
+    n = min(n, units, 4096)
+    sample = rng.choice(units, size=n, replace=False)
+    work = [unit_args(u) for u in sample]
+    ctx = mp.get_context("fork")
+    with ctx.Pool(procs, initializer=_pool_init) as pool:
+        t0 = time.perf_counter()
+        pool.map(_oracle_unit, work, chunksize=1)
+        wall = time.perf_counter() - t0
+    est_total = wall * units / n
+    tokens = shape.num_seqs * shape.window
+    return {"value": tokens / est_total, "unit": "window tokens/s", "cores": procs, "kind": "oracle",
+            "sample": f"{n} of {units} units (seeded), fp64 numpy score+select+compact per unit, "
+                      f"{procs} worker processes x 1 BLAS thread, {wall:.1f} s wall; extrapolated linearly "
+                      f"to all units"}
+
+
+# ----------------------------------------------------------------------------- main
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only: the step has no cross-GPU work (units shard with no exchange); "
+              f"got --gpus {a.gpus}", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from decode_kv_cache_amd import kara as K
+    from decode_kv_cache_amd.workloads import make_workload, shape_by_name
+
+    shape = shape_by_name(a.workload)
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {shape.name} ({shape.description})")
+    t0 = time.time()
+    wl = make_workload(shape, dev)
+    torch.cuda.synchronize()
+    log(f"[bench] generated in {time.time() - t0:.1f} s; pool {wl.k_pool.numel() * wl.k_pool.element_size() / 1e9:.1f} GB x2")
+    cfg = K.make_config(shape, max_blocks_per_seq=wl.max_blocks, num_blocks=wl.num_blocks)
+    S, Lyr, Hkv, W, B = shape.num_seqs, shape.num_layers, shape.num_kv_heads, shape.window, shape.budget
+    scores = torch.empty((S, Lyr, Hkv, W), dtype=torch.float32, device=dev)
+    kept = torch.empty((S, Lyr, Hkv, B), dtype=torch.int32, device=dev)
+    ws = torch.empty((K.kara_workspace_bytes(cfg) + 255) // 4 + 64, dtype=torch.float32, device=dev)
+    seq_lens = torch.empty(S, dtype=torch.int32, device=dev)
+    freed = torch.empty((S, K.kara_max_freed(cfg)), dtype=torch.int32, device=dev)
+    nfreed = torch.empty(S, dtype=torch.int32, device=dev)
+
+    # pristine copy of every block a window touches, and of the tables
+    bs = shape.block_size
+    blocks = []
+    for n in range(S):
+        L = int(wl.host_prior_lens[n])
+        blocks.extend(wl.host_tables[n, L // bs: -(-(L + W) // bs)].tolist())
+    blk_idx = torch.tensor(blocks, dtype=torch.int64, device=dev)
+    k_save = wl.k_pool.index_select(1, blk_idx)
+    v_save = wl.v_pool.index_select(1, blk_idx)
+    tables_save = wl.block_tables.clone()
+
+    st = torch.cuda.Stream(device=dev)
+    def restore():
+        with torch.cuda.stream(st):
+            wl.k_pool.index_copy_(1, blk_idx, k_save)
+            wl.v_pool.index_copy_(1, blk_idx, v_save)
+            wl.block_tables.copy_(tables_save)
+
+    def step(e=None):
+        if e:
+            e[0].record(st)
+        K.kara_score_window(cfg, wl.q, wl.k_pool, wl.block_tables, wl.prior_lens, scores, ws, st)
+        if e:
+            e[1].record(st)
+        K.kara_select_chunks(cfg, scores, kept, None, st)
+        if e:
+            e[2].record(st)
+        K.kara_compact_paged(cfg, wl.k_pool, wl.v_pool, wl.block_tables, wl.prior_lens, seq_lens, kept, freed,
+                             nfreed, st)
+        if e:
+            e[3].record(st)
+
+    for _ in range(a.warmup):
+        restore()
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
+    log(f"[bench] timing {a.steps} steps")
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(a.steps):
+        restore()
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    t_score = [e[0].elapsed_time(e[1]) for e in events]
+    t_sel = [e[1].elapsed_time(e[2]) for e in events]
+    t_cmp = [e[2].elapsed_time(e[3]) for e in events]
+    ms = [x + y + z for x, y, z in zip(t_score, t_sel, t_cmp)]
+    ms_step = float(np.mean(ms))
+    tokens = S * W
+    value = tokens / (ms_step / 1e3)
+    log(f"[bench] step {ms_step:.3f} ms (score {np.mean(t_score):.3f}, select {np.mean(t_sel):.3f}, "
+        f"compact {np.mean(t_cmp):.3f}); wall incl. restores {wall / a.steps * 1e3:.3f} ms/step")
+
+    # roofline of the dominant call (scoring: one Q K^T per unit)
+    G, d = shape.group, shape.head_dim
+    flops = 2.0 * G * W * W * d * shape.units
+    t_s = float(np.mean(t_score)) / 1e3
+    achieved = flops / t_s / 1e12
+    peak = PEAK_TFLOPS[shape.dtype]
+    khash = kernel_source_hash()
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": measured_traffic(shape.name, khash),
+            "kernel": "kara_score_window (row_lse_kernel + col_mass_kernel)",
+            "algorithmic": f"2*G*W^2*d = {2 * G * W * W * d:.4g} FLOP per unit x {shape.units} units"}
+    cbytes = 4.0 * B * d * shape.elem_bytes * shape.units
+    t_c = float(np.mean(t_cmp)) / 1e3
+    compact_roof = {"bound": "hbm", "achieved": round(cbytes / t_c / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(cbytes / t_c / 1e9 / PEAK_HBM_GBS, 4),
+                    "algorithmic": f"4*B*d*elem = {4 * B * d * shape.elem_bytes} B per unit x {shape.units} units"}
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on a CPU sample")
+        cpu = cpu_baseline(wl, shape, a.cpu_seconds)
+        log(f"[bench] cpu baseline {cpu['value']:.1f} tokens/s ({cpu['sample']})")
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "window tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": shape.dtype, "data": "synthetic",
+        "config": {"workload": shape.name, "num_seqs": S, "num_layers": Lyr, "num_q_heads": shape.num_q_heads,
+                   "num_kv_heads": Hkv, "head_dim": d, "window": W, "budget": B, "seeds": shape.seeds,
+                   "radius": shape.radius, "block_size": bs, "prior": list(shape.prior),
+                   "key_model": shape.key_model, "plants": shape.plants, "parallelism": "single GPU"},
+        "stages_ms": {"score": round(float(np.mean(t_score)), 4), "select": round(float(np.mean(t_sel)), 4),
+                      "compact": round(float(np.mean(t_cmp)), 4)},
+        "roofline": roof,
+        "compact_roofline": compact_roof,
+        "cpu_baseline": cpu,
+        "kernel_hash": khash,
+        "wall_ms_per_step_incl_restore": round(wall / a.steps * 1e3, 3),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

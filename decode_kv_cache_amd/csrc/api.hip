@@ -1,0 +1,147 @@
+// Host side of the C ABI declared in include/kara.h: argument checks,
+// geometry, and the launches of the gfx950 kernels.
+#include <math.h>
+
+#include "kara_device.h"
+
+namespace kara {
+hipError_t launch_score(const Geo& g, int dtype, const void* q, const void* kc, const int32_t* tables,
+                        const int32_t* prior, float* scores, float* ws, hipStream_t st);
+size_t score_workspace_bytes(const Geo& g);
+hipError_t launch_select(const Geo& g, const float* scores, int32_t* kept, uint8_t* mask, hipStream_t st);
+hipError_t launch_compact(const Geo& g, int dtype, void* kc, void* vc, int32_t* tables, const int32_t* prior,
+                          int32_t* seq_lens, const int32_t* kept, int32_t* freed, int32_t* num_freed,
+                          int max_freed, hipStream_t st);
+hipError_t launch_validate(const Geo& g, const int32_t* tables, const int32_t* prior, int32_t* bad,
+                           hipStream_t st);
+}  // namespace kara
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int check(const kara_config* c) {
+  if (!c) return KARA_ENULL;
+  if (c->num_seqs < 0 || c->num_layers < 1 || c->num_q_heads < 1 || c->num_kv_heads < 1) return KARA_EINVAL;
+  if (c->num_q_heads % c->num_kv_heads) return KARA_EINVAL;
+  if (c->head_dim != 64 && c->head_dim != 128) return KARA_EINVAL;
+  if (c->window < 1 || c->window > 8192) return KARA_EINVAL;
+  if (c->budget < 1 || c->budget > c->window) return KARA_EINVAL;
+  if (c->seeds < 0 || c->radius < 0 || c->radius > c->window) return KARA_EINVAL;
+  if ((long long)c->seeds * (2LL * c->radius + 1) > c->budget) return KARA_EINVAL;
+  if (!pow2(c->block_size) || c->block_size > 256) return KARA_EINVAL;
+  if (c->dtype != KARA_BF16 && c->dtype != KARA_F32) return KARA_EINVAL;
+  if (c->max_blocks_per_seq < 1 || c->num_blocks < 1) return KARA_EINVAL;
+  if ((long long)c->window > (long long)c->max_blocks_per_seq * c->block_size) return KARA_EINVAL;
+  const long long units = (long long)c->num_seqs * c->num_layers * c->num_kv_heads;
+  if (units > 0x3fffffffLL) return KARA_EINVAL;
+  return KARA_OK;
+}
+
+kara::Geo geo(const kara_config* c) {
+  kara::Geo g;
+  g.S = c->num_seqs;
+  g.Lyr = c->num_layers;
+  g.Hq = c->num_q_heads;
+  g.Hkv = c->num_kv_heads;
+  g.G = c->num_q_heads / c->num_kv_heads;
+  g.D = c->head_dim;
+  g.W = c->window;
+  g.B = c->budget;
+  g.seeds = c->seeds;
+  g.radius = c->radius;
+  g.bs = c->block_size;
+  g.bs_shift = __builtin_ctz((unsigned)c->block_size);
+  g.max_blocks = c->max_blocks_per_seq;
+  g.nblocks = c->num_blocks;
+  g.GW = g.G * g.W;
+  g.GWp = (g.GW + 31) & ~31;
+  g.alpha = (float)(1.4426950408889634 / sqrt((double)g.D));
+  return g;
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return KARA_OK;
+  g_last_hip = (int)e;
+  return KARA_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kara_check_config(const kara_config* cfg) {
+  const int s = check(cfg);
+  return s == KARA_ENULL ? KARA_EINVAL : s;
+}
+
+size_t kara_workspace_bytes(const kara_config* cfg) {
+  if (check(cfg) != KARA_OK) return 0;
+  return kara::score_workspace_bytes(geo(cfg));
+}
+
+int32_t kara_max_freed(const kara_config* cfg) {
+  if (check(cfg) != KARA_OK) return 0;
+  return (cfg->window + cfg->block_size - 1) / cfg->block_size + 1;
+}
+
+int kara_score_window(const kara_config* cfg, const void* q, const void* k_cache, const int32_t* block_tables,
+                      const int32_t* prior_lens, float* scores, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  int s = check(cfg);
+  if (s) return s;
+  if (cfg->num_seqs == 0) return KARA_OK;
+  if (!q || !k_cache || !block_tables || !prior_lens || !scores) return KARA_ENULL;
+  const kara::Geo g = geo(cfg);
+  const size_t need = kara::score_workspace_bytes(g);
+  if (need && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255))) return KARA_EWORKSPACE;
+  return hip_status(kara::launch_score(g, cfg->dtype, q, k_cache, block_tables, prior_lens, scores,
+                                       (float*)workspace, (hipStream_t)stream));
+}
+
+int kara_select_chunks(const kara_config* cfg, const float* scores, int32_t* kept, uint8_t* mask, void* stream) {
+  int s = check(cfg);
+  if (s) return s;
+  if (cfg->num_seqs == 0) return KARA_OK;
+  if (!scores || !kept) return KARA_ENULL;
+  return hip_status(kara::launch_select(geo(cfg), scores, kept, mask, (hipStream_t)stream));
+}
+
+int kara_compact_paged(const kara_config* cfg, void* k_cache, void* v_cache, int32_t* block_tables,
+                       const int32_t* prior_lens, int32_t* seq_lens, const int32_t* kept, int32_t* freed_blocks,
+                       int32_t* num_freed, void* stream) {
+  int s = check(cfg);
+  if (s) return s;
+  if (cfg->num_seqs == 0) return KARA_OK;
+  if (!k_cache || !v_cache || !block_tables || !prior_lens || !seq_lens || !kept || !freed_blocks || !num_freed)
+    return KARA_ENULL;
+  return hip_status(kara::launch_compact(geo(cfg), cfg->dtype, k_cache, v_cache, block_tables, prior_lens,
+                                         seq_lens, kept, freed_blocks, num_freed, kara_max_freed(cfg),
+                                         (hipStream_t)stream));
+}
+
+int kara_validate_tables(const kara_config* cfg, const int32_t* block_tables, const int32_t* prior_lens,
+                         int32_t* bad_seqs, void* stream) {
+  int s = check(cfg);
+  if (s) return s;
+  if (!bad_seqs || (cfg->num_seqs > 0 && (!block_tables || !prior_lens))) return KARA_ENULL;
+  return hip_status(kara::launch_validate(geo(cfg), block_tables, prior_lens, bad_seqs, (hipStream_t)stream));
+}
+
+const char* kara_status_str(int status) {
+  switch (status) {
+    case KARA_OK: return "ok";
+    case KARA_EINVAL: return "invalid configuration or argument";
+    case KARA_ENULL: return "required pointer is NULL";
+    case KARA_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case KARA_EHIP: return "HIP runtime error while enqueueing";
+    case KARA_ENOTIMPL: return "not supported by this build";
+    default: return "unknown status";
+  }
+}
+
+int kara_last_hip_error(void) { return g_last_hip; }
+
+}  // extern "C"

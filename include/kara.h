@@ -1,0 +1,158 @@
+/*
+ * kara.h - C ABI of the Kara decode-time window-compression step on MI355X (gfx950).
+ *
+ * Kara ("Kara: Efficient Reasoning LLM Serving via Sliding-Window KV Cache
+ * Compression", authors' English abstract and section 方法详解 of its
+ * shd-paper.top summary page) compresses, while decoding, only the most recent
+ * window of generated tokens: it scores the window's KV pairs with
+ * bidirectional attention, selects informative ones, grows a subset of them
+ * into chunks (Token2Chunk) and keeps the result in a PagedAttention cache.
+ *
+ * One "unit" is (sequence n, layer l, KV head g).  For every unit the step
+ *   1. kara_score_window  : c[j] = sum_{h in group g} sum_{i<W} softmax_j'(q[h,i].k[j']/sqrt(d))[j]
+ *   2. kara_select_chunks : seeds = first `seeds` positions of the order (c desc, position asc);
+ *                           chunks = [p-radius, p+radius] clipped to the window, merged;
+ *                           fill the rest of `budget` with the best positions outside the chunks;
+ *                           kept = ascending list of exactly `budget` window positions
+ *   3. kara_compact_paged : slot L+r <- slot L+kept[r] (K and V, in place), then every
+ *                           sequence's block table drops the blocks past L+budget.
+ * The score, the Token2Chunk rule and the in-place layout are the readings this
+ * library records where the pages give no formula (see the design notes).
+ *
+ * Conventions for every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    allocates nothing, keeps no state between calls and is reentrant.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
+ *    work and return; results are ready when the stream reaches them.
+ *  - Arguments are checked on the host before anything is enqueued: a call that
+ *    returns an error has enqueued nothing and written nothing.
+ *  - Device-side contents (block ids, prior lengths, kept lists) are not
+ *    checked by the three step calls.  Kernels never access memory outside the
+ *    buffers the configuration describes: a slot whose table entry is out of
+ *    range is skipped, so the outputs for that sequence are unspecified.
+ *    kara_validate_tables reports such entries.
+ *
+ * Layouts (row-major, contiguous, element type = cfg.dtype unless stated):
+ *   q            [num_seqs][num_layers][window][num_q_heads][head_dim]  window queries
+ *   k_cache,
+ *   v_cache      [num_layers][num_blocks][num_kv_heads][block_size][head_dim]
+ *   block_tables int32 [num_seqs][max_blocks_per_seq]; logical block b of sequence n
+ *                lives in physical block block_tables[n][b]
+ *   prior_lens   int32 [num_seqs]: L, tokens before the window; the window is the
+ *                logical slots [L, L+window)
+ *   scores       float [num_seqs][num_layers][num_kv_heads][window]
+ *   kept         int32 [num_seqs][num_layers][num_kv_heads][budget], window-relative
+ *   mask         uint8 [num_seqs][num_layers][num_kv_heads][window] (optional)
+ *   freed_blocks int32 [num_seqs][kara_max_freed(cfg)], -1 padded
+ *   num_freed    int32 [num_seqs];  seq_lens int32 [num_seqs] (out: L + budget)
+ * Query head h belongs to KV head h / (num_q_heads / num_kv_heads).
+ */
+#ifndef KARA_H_
+#define KARA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define KARA_OK 0
+#define KARA_EINVAL (-1)     /* a configuration value or constraint is violated */
+#define KARA_ENULL (-2)      /* a required pointer is NULL */
+#define KARA_EWORKSPACE (-3) /* workspace missing or smaller than kara_workspace_bytes */
+#define KARA_EHIP (-4)       /* the HIP runtime reported an error while enqueueing */
+#define KARA_ENOTIMPL (-5)   /* valid request this build does not support */
+
+/* element types of q, k_cache and v_cache */
+#define KARA_BF16 0
+#define KARA_F32 1
+
+typedef struct kara_config {
+  int32_t num_seqs;      /* >= 0 (0 = nothing to do) */
+  int32_t num_layers;    /* >= 1 */
+  int32_t num_q_heads;   /* >= 1, multiple of num_kv_heads */
+  int32_t num_kv_heads;  /* >= 1 */
+  int32_t head_dim;      /* 64 or 128 */
+  int32_t window;        /* W, 1..8192 */
+  int32_t budget;        /* B, 1..W */
+  int32_t seeds;         /* s >= 0 */
+  int32_t radius;        /* r >= 0, with s*(2r+1) <= B */
+  int32_t block_size;    /* power of two, 1..256 */
+  int32_t dtype;         /* KARA_BF16 or KARA_F32 */
+  int32_t max_blocks_per_seq; /* >= 1, columns of block_tables */
+  int64_t num_blocks;    /* >= 1, physical blocks per layer in k_cache / v_cache */
+} kara_config;
+
+/* Checks a configuration on the host; returns KARA_OK or KARA_EINVAL. */
+int kara_check_config(const kara_config* cfg);
+
+/* Bytes of device workspace kara_score_window needs for cfg (0 if none);
+ * returns 0 for an invalid cfg. */
+size_t kara_workspace_bytes(const kara_config* cfg);
+
+/* Columns of freed_blocks: the most blocks one sequence can free, ceil(W/bs)+1. */
+int32_t kara_max_freed(const kara_config* cfg);
+
+/*
+ * Step 1 - window scores (bidirectional in-window attention; Kara abstract).
+ * For every unit writes scores[n][l][g][j] = c[j] as defined above, in fp32.
+ * Reads q and the window rows of k_cache through block_tables; q, k_cache,
+ * block_tables and prior_lens are not modified.  `workspace` must hold
+ * kara_workspace_bytes(cfg) bytes (256-byte aligned); its contents on entry
+ * are ignored.  Errors: KARA_EINVAL, KARA_ENULL, KARA_EWORKSPACE, KARA_EHIP.
+ */
+int kara_score_window(const kara_config* cfg, const void* q, const void* k_cache,
+                      const int32_t* block_tables, const int32_t* prior_lens, float* scores,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Step 2 - Token2Chunk selection (Kara abstract: a subset of the selected KV
+ * pairs is expanded into chunks).  For every unit reads scores[n][l][g][:] and
+ * writes the `budget` kept window positions, strictly ascending, to kept.  If
+ * mask is not NULL it also writes mask[..][j] = 1 for kept j, else 0.  The
+ * order compares scores as IEEE floats (-0 equals +0) and breaks ties by the
+ * lower position; scores must not be NaN.  Errors: KARA_EINVAL, KARA_ENULL,
+ * KARA_EHIP.
+ */
+int kara_select_chunks(const kara_config* cfg, const float* scores, int32_t* kept, uint8_t* mask,
+                       void* stream);
+
+/*
+ * Step 3 - in-place compaction into PagedAttention blocks (Kara abstract: the
+ * method is adapted to PagedAttention and lowers KV memory).  For every unit
+ * and r < budget, the K and V rows of logical slot L+r become the old rows of
+ * slot L+kept[r] (all old rows are read before any is overwritten; kept must
+ * be strictly ascending in [0, window)).  Then, per sequence, the entries of
+ * logical blocks ceil((L+B)/bs) .. ceil((L+W)/bs)-1 are copied in that order
+ * to freed_blocks[n][..] (rest -1), set to -1 in block_tables, num_freed[n]
+ * gets their count and seq_lens[n] = L + B.  No other byte of k_cache or
+ * v_cache changes.  The caller may reuse freed blocks once the stream has
+ * passed this call.  Errors: KARA_EINVAL, KARA_ENULL, KARA_EHIP.
+ */
+int kara_compact_paged(const kara_config* cfg, void* k_cache, void* v_cache, int32_t* block_tables,
+                       const int32_t* prior_lens, int32_t* seq_lens, const int32_t* kept,
+                       int32_t* freed_blocks, int32_t* num_freed, void* stream);
+
+/*
+ * Debug check of the device-side addressing data: for every sequence, L >= 0,
+ * L + W <= max_blocks_per_seq * block_size, and every table entry of the
+ * logical blocks that hold slots [L - L % bs, L + W) lies in [0, num_blocks).
+ * Writes to *bad_seqs (device int32) the number of sequences that fail.
+ * Errors: KARA_EINVAL, KARA_ENULL, KARA_EHIP.
+ */
+int kara_validate_tables(const kara_config* cfg, const int32_t* block_tables,
+                         const int32_t* prior_lens, int32_t* bad_seqs, void* stream);
+
+/* Short text for a status code (static storage). */
+const char* kara_status_str(int status);
+
+/* HIP error code behind the last KARA_EHIP returned on this thread (0 if none). */
+int kara_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KARA_H_ */

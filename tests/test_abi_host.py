@@ -1,0 +1,101 @@
+"""The C ABI library loads, exports every declared symbol, and validates its
+arguments on the host (no GPU needed: every call here returns before any HIP
+call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from decode_kv_cache_amd import kara as K
+from decode_kv_cache_amd.workloads import SHAPES, shape_by_name
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "kara.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kara_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = K.lib()
+    names = _declared()
+    assert len(names) >= 9
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(K.EXPORTED_SYMBOLS)
+
+
+def _cfg(name="llama8b_b64", **kw):
+    s = shape_by_name(name)
+    c = K.make_config(s, max_blocks_per_seq=4096, num_blocks=100000)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_all_benchmark_shapes_are_valid():
+    for s in SHAPES:
+        assert K.kara_check_config(K.make_config(s, max_blocks_per_seq=4096, num_blocks=10)) == 0, s.name
+
+
+@pytest.mark.parametrize("field,value", [
+    ("num_seqs", -1), ("num_layers", 0), ("num_q_heads", 0), ("num_kv_heads", 0), ("num_q_heads", 30),
+    ("head_dim", 96), ("head_dim", 256), ("window", 0), ("window", 8193), ("budget", 0), ("budget", 1025),
+    ("seeds", -1), ("radius", -1), ("seeds", 20), ("block_size", 12), ("block_size", 512), ("dtype", 7),
+    ("max_blocks_per_seq", 0), ("num_blocks", 0), ("max_blocks_per_seq", 63),
+])
+def test_invalid_config_fields(field, value):
+    assert K.kara_check_config(_cfg(**{field: value})) == -1
+
+
+def test_seed_span_constraint_is_exact():
+    assert K.kara_check_config(_cfg(seeds=17, radius=5, budget=187)) == 0      # 17 * 11 = 187
+    assert K.kara_check_config(_cfg(seeds=17, radius=5, budget=186)) == -1
+
+
+def test_workspace_bytes_and_max_freed():
+    c = _cfg()
+    units = 64 * 32 * 8
+    assert K.kara_workspace_bytes(c) == units * 4 * 1024 * 4
+    c2 = _cfg(num_q_heads=28, num_kv_heads=4, window=33, budget=20, seeds=1)   # G*W = 231 -> 256 rows
+    assert K.kara_workspace_bytes(c2) == 64 * 32 * 4 * 256 * 4
+    assert K.kara_max_freed(c) == 1024 // 16 + 1
+    assert K.kara_max_freed(_cfg(window=100, budget=90, block_size=32)) == 4 + 1
+    assert K.kara_workspace_bytes(_cfg(window=0)) == 0
+    assert K.kara_max_freed(_cfg(window=0)) == 0
+
+
+def test_entry_points_reject_before_any_device_work():
+    lib = K.lib()
+    bad = _cfg(budget=5000)
+    good = _cfg()
+    n = None
+    assert lib.kara_score_window(ctypes.byref(bad), n, n, n, n, n, n, 0, n) == -1
+    assert lib.kara_select_chunks(ctypes.byref(bad), n, n, n, n) == -1
+    assert lib.kara_compact_paged(ctypes.byref(bad), n, n, n, n, n, n, n, n, n) == -1
+    assert lib.kara_validate_tables(ctypes.byref(bad), n, n, n, n) == -1
+    assert lib.kara_score_window(ctypes.byref(good), n, n, n, n, n, n, 0, n) == -2
+    assert lib.kara_select_chunks(ctypes.byref(good), n, n, n, n) == -2
+    assert lib.kara_compact_paged(ctypes.byref(good), n, n, n, n, n, n, n, n, n) == -2
+    assert lib.kara_validate_tables(ctypes.byref(good), n, n, n, n) == -2
+    assert lib.kara_score_window(None, n, n, n, n, n, n, 0, n) == -2
+    # workspace: a non-null fake pointer that is too small or misaligned never reaches the device
+    p = ctypes.c_void_p(0x1000)
+    assert lib.kara_score_window(ctypes.byref(good), p, p, p, p, p, p, 10, n) == -3
+    assert lib.kara_score_window(ctypes.byref(good), p, p, p, p, p, ctypes.c_void_p(0x1010),
+                                 K.kara_workspace_bytes(good), n) == -3
+    # an empty batch is a no-op that touches nothing
+    empty = _cfg(num_seqs=0)
+    assert lib.kara_score_window(ctypes.byref(empty), n, n, n, n, n, n, 0, n) == 0
+    assert lib.kara_select_chunks(ctypes.byref(empty), n, n, n, n) == 0
+    assert lib.kara_compact_paged(ctypes.byref(empty), n, n, n, n, n, n, n, n, n) == 0
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5, 99):
+        assert isinstance(K.kara_status_str(code), str) and K.kara_status_str(code)
+    assert K.kara_last_hip_error() == 0
