@@ -19,6 +19,12 @@ SOURCES = ["api.hip", "score.hip", "select.hip", "compact.hip"]
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the softmax arithmetic reads them directly
+    # instead of copying each one out of an AGPR first
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # scores, logits and weights are never NaN: max/min need no quieting of
+    # their operands (infinities stay honoured; the kernels rely on them)
+    "-fno-honor-nans",
     "-Wno-unused-result",
 ]
 
@@ -30,11 +36,11 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = True) -> str:
+def build(verbose: bool = True, out: str = LIB, csrc: str = CSRC, extra=()) -> str:
     """Compile every HIP source into libkara.so next to this file; return its path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}",
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, f"-I{INCLUDE}", f"-I{csrc}",
+           *[os.path.join(csrc, s) for s in SOURCES], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -44,8 +50,8 @@ def build(verbose: bool = True) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -33,7 +33,9 @@ int check(const kara_config* c) {
   if ((long long)c->seeds * (2LL * c->radius + 1) > c->budget) return KARA_EINVAL;
   if (!pow2(c->block_size) || c->block_size > 256) return KARA_EINVAL;
   if (c->dtype != KARA_BF16 && c->dtype != KARA_F32) return KARA_EINVAL;
-  if (c->max_blocks_per_seq < 1 || c->num_blocks < 1) return KARA_EINVAL;
+  if (c->max_blocks_per_seq < 1 || c->num_blocks < 0) return KARA_EINVAL;
+  if (c->num_seqs > 0 && c->num_blocks < 1) return KARA_EINVAL;   // a window needs at least one block
+  if (c->num_blocks > 0x7fffffffLL) return KARA_EINVAL;            // block ids are int32
   if ((long long)c->window > (long long)c->max_blocks_per_seq * c->block_size) return KARA_EINVAL;
   const long long units = (long long)c->num_seqs * c->num_layers * c->num_kv_heads;
   if (units > 0x3fffffffLL) return KARA_EINVAL;

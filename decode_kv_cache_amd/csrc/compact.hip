@@ -18,7 +18,7 @@
 namespace kara {
 
 constexpr int CMP_THREADS = 256;
-constexpr int CMP_VEC = 8;   // 16-byte vectors per thread per chunk
+constexpr int CMP_VEC = 16;  // 16-byte vectors per thread per chunk (256 rows of 256 B)
 
 template <int ROWBYTES>
 __global__ __launch_bounds__(CMP_THREADS) void compact_kernel(Geo g, unsigned char* __restrict__ kc,

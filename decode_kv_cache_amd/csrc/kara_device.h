@@ -89,6 +89,44 @@ __device__ inline long long slot_offset(const Geo& g, const int32_t* __restrict_
   return ((((long long)layer * g.nblocks + blk) * g.Hkv + kvh) * g.bs + off) * (long long)g.D;
 }
 
+// Paged addressing for hot loops, in bytes.  `blk_stride` is the byte size
+// of one physical block (Hkv * bs * D elements) and `base` the byte offset of
+// (layer, kv head, slot 0) inside block 0.  The table read is clamped into the
+// row and an out-of-range entry is replaced by block 0 (which exists whenever
+// there is a sequence), so the address is always inside the pool; the data of
+// such a slot is unspecified.
+struct PagedRows {
+  const int32_t* trow;
+  unsigned long long base;
+  uint32_t blk_stride, row_bytes;
+  int L, bs_shift, bs_mask, max_blocks;
+  uint32_t nblocks;
+};
+
+// Byte offset of logical slot `pos` (see PagedRows).
+__device__ __forceinline__ unsigned long long paged_row(const PagedRows p, int pos) {
+  const int lb = min(max(pos >> p.bs_shift, 0), p.max_blocks - 1);
+  const int32_t blk = p.trow[lb];
+  const uint32_t b = (uint32_t)blk < p.nblocks ? (uint32_t)blk : 0u;
+  return (unsigned long long)b * p.blk_stride + p.base + (uint32_t)((pos & p.bs_mask) * p.row_bytes);
+}
+
+__device__ inline PagedRows paged_rows(const Geo& g, const int32_t* table_row, int layer, int kvh, int L,
+                                       int elem_bytes) {
+  PagedRows p;
+  p.trow = table_row;
+  p.blk_stride = (uint32_t)(g.Hkv * g.bs * g.D * elem_bytes);
+  p.row_bytes = (uint32_t)(g.D * elem_bytes);
+  p.base = (unsigned long long)layer * (unsigned long long)g.nblocks * p.blk_stride +
+           (unsigned long long)kvh * g.bs * p.row_bytes;
+  p.L = L;
+  p.bs_shift = g.bs_shift;
+  p.bs_mask = g.bs - 1;
+  p.max_blocks = g.max_blocks;
+  p.nblocks = (uint32_t)g.nblocks;
+  return p;
+}
+
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -200,7 +200,7 @@ def make_workload(shape: KaraShape, device="cpu", *, canary=True) -> Workload:
     prior = _prior_lens(shape)
     nblk = [-(-(int(prior[n]) + W) // bs) for n in range(S)]
     num_blocks = int(sum(nblk))
-    max_blocks = max(nblk) if nblk else 1
+    max_blocks = max(nblk) if nblk else -(-W // bs)
     perm = np.random.default_rng(_seed(shape.shape_id, 0xB10C, 1)).permutation(num_blocks)
     tables = np.full((max(S, 0), max_blocks), -1, dtype=np.int32)
     pos = 0

@@ -46,7 +46,7 @@ def test_all_benchmark_shapes_are_valid():
     ("num_seqs", -1), ("num_layers", 0), ("num_q_heads", 0), ("num_kv_heads", 0), ("num_q_heads", 30),
     ("head_dim", 96), ("head_dim", 256), ("window", 0), ("window", 8193), ("budget", 0), ("budget", 1025),
     ("seeds", -1), ("radius", -1), ("seeds", 20), ("block_size", 12), ("block_size", 512), ("dtype", 7),
-    ("max_blocks_per_seq", 0), ("num_blocks", 0), ("max_blocks_per_seq", 63),
+    ("max_blocks_per_seq", 0), ("num_blocks", -1), ("max_blocks_per_seq", 63),
 ])
 def test_invalid_config_fields(field, value):
     assert K.kara_check_config(_cfg(**{field: value})) == -1
