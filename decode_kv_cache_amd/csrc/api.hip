@@ -7,7 +7,7 @@
 namespace kara {
 hipError_t launch_score(const Geo& g, int dtype, const void* q, const void* kc, const int32_t* tables,
                         const int32_t* prior, float* scores, float* ws, hipStream_t st);
-size_t score_workspace_bytes(const Geo& g);
+size_t score_workspace_bytes(const Geo& g, int dtype);
 hipError_t launch_select(const Geo& g, const float* scores, int32_t* kept, uint8_t* mask, hipStream_t st);
 hipError_t launch_compact(const Geo& g, int dtype, void* kc, void* vc, int32_t* tables, const int32_t* prior,
                           int32_t* seq_lens, const int32_t* kept, int32_t* freed, int32_t* num_freed,
@@ -81,7 +81,7 @@ int kara_check_config(const kara_config* cfg) {
 
 size_t kara_workspace_bytes(const kara_config* cfg) {
   if (check(cfg) != KARA_OK) return 0;
-  return kara::score_workspace_bytes(geo(cfg));
+  return kara::score_workspace_bytes(geo(cfg), cfg->dtype);
 }
 
 int32_t kara_max_freed(const kara_config* cfg) {
@@ -97,7 +97,7 @@ int kara_score_window(const kara_config* cfg, const void* q, const void* k_cache
   if (cfg->num_seqs == 0) return KARA_OK;
   if (!q || !k_cache || !block_tables || !prior_lens || !scores) return KARA_ENULL;
   const kara::Geo g = geo(cfg);
-  const size_t need = kara::score_workspace_bytes(g);
+  const size_t need = kara::score_workspace_bytes(g, cfg->dtype);
   if (need && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255))) return KARA_EWORKSPACE;
   return hip_status(kara::launch_score(g, cfg->dtype, q, k_cache, block_tables, prior_lens, scores,
                                        (float*)workspace, (hipStream_t)stream));

@@ -18,6 +18,8 @@
 namespace kara {
 
 constexpr int CMP_THREADS = 256;
+// rows are streamed once: non-temporal loads and stores keep them out of the caches
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int CMP_VEC = 16;  // 16-byte vectors per thread per chunk (256 rows of 256 B)
 
 template <int ROWBYTES>
@@ -41,7 +43,7 @@ __global__ __launch_bounds__(CMP_THREADS) void compact_kernel(Geo g, unsigned ch
   const int part = t % TPR;
   const int rsub = t / TPR;
   for (int c0 = 0; c0 < g.B; c0 += CH) {
-    uint4 buf[CMP_VEC];
+    u32x4 buf[CMP_VEC];
     long long dst[CMP_VEC];
 #pragma unroll
     for (int v = 0; v < CMP_VEC; ++v) {
@@ -52,7 +54,7 @@ __global__ __launch_bounds__(CMP_THREADS) void compact_kernel(Geo g, unsigned ch
         const long long so = (j >= 0 && j < g.W) ? slot_offset(g, trow, layer, kvh, L + j) : -1;
         const long long d = slot_offset(g, trow, layer, kvh, L + r);
         if (so >= 0 && d >= 0) {
-          buf[v] = *reinterpret_cast<const uint4*>(pool + so * esize + part * 16);
+          buf[v] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pool + so * esize + part * 16));
           dst[v] = d;
         }
       }
@@ -61,7 +63,7 @@ __global__ __launch_bounds__(CMP_THREADS) void compact_kernel(Geo g, unsigned ch
     __syncthreads();
 #pragma unroll
     for (int v = 0; v < CMP_VEC; ++v)
-      if (dst[v] >= 0) *reinterpret_cast<uint4*>(pool + dst[v] * esize + part * 16) = buf[v];
+      if (dst[v] >= 0) __builtin_nontemporal_store(buf[v], reinterpret_cast<u32x4*>(pool + dst[v] * esize + part * 16));
   }
 }
 

@@ -60,9 +60,15 @@ def test_seed_span_constraint_is_exact():
 def test_workspace_bytes_and_max_freed():
     c = _cfg()
     units = 64 * 32 * 8
-    assert K.kara_workspace_bytes(c) == units * 4 * 1024 * 4
-    c2 = _cfg(num_q_heads=28, num_kv_heads=4, window=33, budget=20, seeds=1)   # G*W = 231 -> 256 rows
+    # bf16, head_dim 128, W <= 1024: single-pass scorer, no workspace
+    assert K.kara_workspace_bytes(c) == 0
+    # two-pass scorer: one fp32 log-sum-exp per query row, rows padded to 32
+    c1 = _cfg(window=2048)
+    assert K.kara_workspace_bytes(c1) == units * 4 * 2048 * 4
+    c2 = _cfg(num_q_heads=28, num_kv_heads=4, window=33, budget=20, seeds=1, head_dim=64)   # G*W = 231 -> 256
     assert K.kara_workspace_bytes(c2) == 64 * 32 * 4 * 256 * 4
+    c3 = _cfg(dtype=1)
+    assert K.kara_workspace_bytes(c3) == units * 4 * 1024 * 4
     assert K.kara_max_freed(c) == 1024 // 16 + 1
     assert K.kara_max_freed(_cfg(window=100, budget=90, block_size=32)) == 4 + 1
     assert K.kara_workspace_bytes(_cfg(window=0)) == 0
@@ -72,7 +78,7 @@ def test_workspace_bytes_and_max_freed():
 def test_entry_points_reject_before_any_device_work():
     lib = K.lib()
     bad = _cfg(budget=5000)
-    good = _cfg()
+    good = _cfg(window=2048)          # a configuration whose scorer needs a workspace
     n = None
     assert lib.kara_score_window(ctypes.byref(bad), n, n, n, n, n, n, 0, n) == -1
     assert lib.kara_select_chunks(ctypes.byref(bad), n, n, n, n) == -1

@@ -139,7 +139,7 @@ def test_validate_tables_flags_bad_sequences():
 
 def test_host_rejects_bad_arguments_before_enqueueing():
     from decode_kv_cache_amd import kara as K
-    wl = make_workload(SMALL[1], "cuda")
+    wl = make_workload(SMALL[3], "cuda")      # head_dim 64: two-pass scorer with a workspace
     cfg = config_of(wl)
     out = Outputs(cfg, "cuda")
     small_ws = torch.empty(16, dtype=torch.float32, device="cuda")
