@@ -222,7 +222,8 @@ def main():
     khash = kernel_source_hash()
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": measured_traffic(shape.name, khash),
-            "kernel": "kara_score_window (row_lse_kernel + col_mass_kernel)",
+            "kernel": ("fused_score_kernel" if K.kara_score_passes(cfg) == 1
+                       else "row_lse_kernel + col_mass_kernel") + " (kara_score_window)",
             "algorithmic": f"2*G*W^2*d = {2 * G * W * W * d:.4g} FLOP per unit x {shape.units} units"}
     cbytes = 4.0 * B * d * shape.elem_bytes * shape.units
     t_c = float(np.mean(t_cmp)) / 1e3

@@ -8,6 +8,7 @@ namespace kara {
 hipError_t launch_score(const Geo& g, int dtype, const void* q, const void* kc, const int32_t* tables,
                         const int32_t* prior, float* scores, float* ws, hipStream_t st);
 size_t score_workspace_bytes(const Geo& g, int dtype);
+bool fused_score_supported(const Geo& g, int dtype);
 hipError_t launch_select(const Geo& g, const float* scores, int32_t* kept, uint8_t* mask, hipStream_t st);
 hipError_t launch_compact(const Geo& g, int dtype, void* kc, void* vc, int32_t* tables, const int32_t* prior,
                           int32_t* seq_lens, const int32_t* kept, int32_t* freed, int32_t* num_freed,
@@ -82,6 +83,11 @@ int kara_check_config(const kara_config* cfg) {
 size_t kara_workspace_bytes(const kara_config* cfg) {
   if (check(cfg) != KARA_OK) return 0;
   return kara::score_workspace_bytes(geo(cfg), cfg->dtype);
+}
+
+int kara_score_passes(const kara_config* cfg) {
+  if (check(cfg) != KARA_OK) return 0;
+  return kara::fused_score_supported(geo(cfg), cfg->dtype) ? 1 : 2;
 }
 
 int32_t kara_max_freed(const kara_config* cfg) {

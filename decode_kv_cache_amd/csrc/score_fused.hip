@@ -12,12 +12,12 @@
 // transposed orientation S^T = K Q^T, so a lane owns one query row and 32 of
 // the wave's keys:
 //   - row max and row sum are lane-local, then merged over the 4 lane groups
-//     that share a row (two shuffles) and over the 8 waves (LDS, one barrier
-//     each);
-//   - the softmax weight of every logit is exp2(x - m) / l with one row
-//     weight 1/l per lane, and the column sums accumulate lane-locally across
-//     all blocks of the unit; they are reduced over the 16 query lanes once,
-//     at the end.
+//     that share a row (two lane swaps) and over the 8 waves (LDS, one
+//     barrier per block);
+//   - every logit's softmax weight is a per-lane scalar times its
+//     exponential, and the column sums accumulate lane-locally across all
+//     blocks of the unit; they are reduced over the 16 query lanes once, at
+//     the end.
 // Each logit is computed once and exponentiated once.
 #include "kara_device.h"
 
@@ -43,68 +43,66 @@ __device__ __forceinline__ f32x4v mfma16(const bf16x8& a, const bf16x8& b, const
 // [32q, 32q+32) of head_dim, 8 elements per instruction, for both operands.
 // Result: lane l holds column l % 16 and rows 4*(l/16) .. +3.
 
-__global__ __launch_bounds__(FTHREADS, 1) void fused_score_kernel(Geo g, const __bf16* __restrict__ q,
-                                                                   const __bf16* __restrict__ kc,
-                                                                   const int32_t* __restrict__ tables,
-                                                                   const int32_t* __restrict__ prior,
-                                                                   float* __restrict__ scores) {
-  __shared__ __align__(16) unsigned char qtile[2][QB * QLROW];
-  __shared__ float red_max[QB][FW];
-  __shared__ float red_sum[QB][FW];
+// max / sum over the 4 lane groups that hold the same query row (lanes l,
+// l^16, l^32, l^48): two lane-swap steps, no LDS traffic
+__device__ __forceinline__ float group_max(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group_sum(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Per block, each wave exponentiates its logits against its own row maximum
+// m_w and publishes (m_w, l_w = sum of its exponentials).  After the one
+// barrier of the block every wave combines the 8 pairs,
+//     m = max_w m_w,   l = sum_w l_w 2^(alpha (m_w - m)),
+// and weights its exponentials by 2^(alpha (m_w - m)) / l, which is the
+// softmax over all W keys of the row.
+template <bool MASK>
+__device__ __forceinline__ void fused_unit(const Geo& g, int unit, const __bf16* __restrict__ q,
+                                           const bf16x8 (&kf)[KTW][4], int key0, unsigned char (*qtile)[QB * QLROW],
+                                           float2 (*red)[QB][FW], float* __restrict__ scores) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int qlane = lane & 15, grp = lane >> 4;
-  const int unit = blockIdx.x;
   const int kvh = unit % g.Hkv;
   const int layer = (unit / g.Hkv) % g.Lyr;
   const int n = unit / (g.Hkv * g.Lyr);
-  const int L = prior[n];
-  const int32_t* trow = tables + (long long)n * g.max_blocks;
-
-  // ---- resident keys: tile t of this wave covers window keys key0 + 16 t + (0..15)
-  const int key0 = wave * KTW * 16;
-  const unsigned char* kbytes = reinterpret_cast<const unsigned char*>(kc);
-  const PagedRows pr = paged_rows(g, trow, layer, kvh, L, 2);
-  bf16x8 kf[KTW][4];
-#pragma unroll
-  for (int t = 0; t < KTW; ++t) {
-    const int j = min(key0 + 16 * t + qlane, g.W - 1);
-    const uint4* src = reinterpret_cast<const uint4*>(kbytes + paged_row(pr, L + j) + grp * 64);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const uint4 v = src[s];
-      __builtin_memcpy(&kf[t][s], &v, 16);
-    }
-  }
-  // keys this lane holds in tile t: key0 + 16 t + 4 grp + r, valid if < W
-  const int kbase = key0 + 4 * grp;
+  const int kbase = key0 + 4 * grp;    // lane holds keys kbase + 16 t + r
 
   // ---- query rows of block b: rows 16 b .. 16 b + 15 of the unit (row = i*G + h)
   const unsigned char* qbytes = reinterpret_cast<const unsigned char*>(
       q + (((long long)n * g.Lyr + layer) * g.W) * g.Hq * FD + (long long)kvh * g.G * FD);
   const int nblk = (g.GW + QB - 1) / QB;
-  // staging: 256 threads move 16 rows x 256 bytes (one 16-byte chunk each)
-  const int srow = (tid >> 4) & 15, sch = tid & 15;
-  auto q_fetch = [&](int b) -> uint4 {
+  // staging: the 512 threads move 16 rows x 256 bytes, 8 bytes each; tiles are
+  // fetched two blocks ahead (two register stages) to cover memory latency
+  const int srow = tid >> 5, sbyte = (tid & 31) * 8;
+  auto q_fetch = [&](int b) -> uint2 {
     const int row = min(b * QB + srow, g.GW - 1);
     const int qi = row / g.G, qh = row - qi * g.G;
-    return *reinterpret_cast<const uint4*>(qbytes + ((long long)qi * g.Hq + qh) * QROWB + sch * 16);
+    return *reinterpret_cast<const uint2*>(qbytes + ((long long)qi * g.Hq + qh) * QROWB + sbyte);
   };
+  auto q_stash = [&](int buf, uint2 v) { *reinterpret_cast<uint2*>(&qtile[buf][srow * QLROW + sbyte]) = v; };
 
   f32x4v colacc[KTW];
 #pragma unroll
   for (int t = 0; t < KTW; ++t) colacc[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
 
-  uint4 pre = make_uint4(0, 0, 0, 0);
-  if (tid < 256) {
-    pre = q_fetch(0);
-    *reinterpret_cast<uint4*>(&qtile[0][srow * QLROW + sch * 16]) = pre;
-  }
+  q_stash(0, q_fetch(0));
+  uint2 stage1 = q_fetch(min(1, nblk - 1));    // tile b+1
   __syncthreads();
   const float alpha = g.alpha;
-  for (int b = 0; b < nblk; ++b) {
+  // one block: consume tile b (in LDS), publish tile b+1 (held in `cur`) and
+  // start fetching tile b+2 into `nxt`
+  auto block = [&](int b, uint2& cur, uint2& nxt) {
     const int buf = b & 1;
-    if (tid < 256) pre = q_fetch(min(b + 1, nblk - 1));
+    nxt = q_fetch(min(b + 2, nblk - 1));
     // B operand: query row qlane of this block, head_dim range [32 grp, 32 grp + 32)
     bf16x8 qf[4];
     {
@@ -115,69 +113,64 @@ __global__ __launch_bounds__(FTHREADS, 1) void fused_score_kernel(Geo g, const _
         __builtin_memcpy(&qf[s], &v, 16);
       }
     }
-    // logits S^T: acc[t][r] = k[key0 + 16t + 4grp + r] . q[row 16b + qlane]
+    // logits S^T: acc[t][r] = k[kbase + 16t + r] . q[row 16b + qlane]
+    // (reduction step outermost: 8 independent MFMAs between dependent ones)
     f32x4v acc[KTW];
 #pragma unroll
-    for (int t = 0; t < KTW; ++t) {
-      f32x4v a = f32x4v{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < KTW; ++t) acc[t] = mfma16(kf[t][0], qf[0], f32x4v{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-      for (int s = 0; s < 4; ++s) a = mfma16(kf[t][s], qf[s], a);
-      acc[t] = a;
-    }
-    // keys past the window (only in the last tiles) do not take part
-    if (key0 + KTW * 16 > g.W) {
+    for (int s = 1; s < 4; ++s)
+#pragma unroll
+      for (int t = 0; t < KTW; ++t) acc[t] = mfma16(kf[t][s], qf[s], acc[t]);
+    if (MASK) {                                  // keys past the window take no part
 #pragma unroll
       for (int t = 0; t < KTW; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (kbase + 16 * t + r >= g.W) acc[t][r] = -INFINITY;
     }
-    // row max: lane-local, then the 4 lane groups, then the 8 waves
-    float mx = fmaxf(acc[0][0], acc[0][1]);
-    mx = fmaxf(mx, fmaxf(acc[0][2], acc[0][3]));
+    // wave-local row max (raw logits)
+    float mx = fmaxf(fmaxf(acc[0][0], acc[0][1]), fmaxf(acc[0][2], acc[0][3]));
 #pragma unroll
-    for (int t = 1; t < KTW; ++t) {
-      mx = fmaxf(mx, fmaxf(acc[t][0], acc[t][1]));
-      mx = fmaxf(mx, fmaxf(acc[t][2], acc[t][3]));
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (lane < 16) red_max[qlane][wave] = mx;
-    __syncthreads();
-    {
-      const f32x4v a = *reinterpret_cast<const f32x4v*>(&red_max[qlane][0]);
-      const f32x4v c = *reinterpret_cast<const f32x4v*>(&red_max[qlane][4]);
-      mx = fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3])));
-    }
-    // exponentials (in place) and row sum; a wave with no valid key has mx = -inf
-    // only if every wave does, which cannot happen (W >= 1)
-    const float moff = -mx * alpha;
-    float sm = 0.f;
+    for (int t = 1; t < KTW; ++t) mx = fmaxf(mx, fmaxf(fmaxf(acc[t][0], acc[t][1]), fmaxf(acc[t][2], acc[t][3])));
+    mx = group_max(mx);
+    const float moff = MASK && mx == -INFINITY ? 0.f : -mx * alpha;
+    float sp[4] = {0.f, 0.f, 0.f, 0.f};          // four partial sums: short dependency chains
 #pragma unroll
     for (int t = 0; t < KTW; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float e = fast_exp2(__builtin_fmaf(acc[t][r], alpha, moff));
         acc[t][r] = e;
-        sm += e;
+        sp[r] += e;
       }
-    sm += __shfl_xor(sm, 16);
-    sm += __shfl_xor(sm, 32);
-    if (lane < 16) red_sum[qlane][wave] = sm;
-    // publish the next query tile before the barrier that ends this block's reads
-    if (tid < 256) *reinterpret_cast<uint4*>(&qtile[buf ^ 1][srow * QLROW + sch * 16]) = pre;
+    const float sm = group_sum((sp[0] + sp[1]) + (sp[2] + sp[3]));
+    if (lane < 16) red[buf][qlane][wave] = make_float2(mx, sm);
+    // publish tile b+1 before the barrier that ends this block's reads
+    q_stash(buf ^ 1, cur);
     __syncthreads();
-    {
-      const f32x4v a = *reinterpret_cast<const f32x4v*>(&red_sum[qlane][0]);
-      const f32x4v c = *reinterpret_cast<const f32x4v*>(&red_sum[qlane][4]);
-      sm = ((a[0] + a[1]) + (a[2] + a[3])) + ((c[0] + c[1]) + (c[2] + c[3]));
+    float m = -INFINITY;
+    float2 pr[FW];
+#pragma unroll
+    for (int w = 0; w < FW; ++w) {
+      pr[w] = red[buf][qlane][w];
+      m = fmaxf(m, pr[w].x);
     }
-    // rows past G*W contribute nothing
-    const float w = (b * QB + qlane < g.GW) ? __builtin_amdgcn_rcpf(sm) : 0.f;
+    float l = 0.f;
+#pragma unroll
+    for (int w = 0; w < FW; ++w) l += pr[w].y * fast_exp2((pr[w].x - m) * alpha);   // m_w = -inf -> 0
+    // this wave's weight; rows past G*W contribute nothing
+    const float own = MASK && mx == -INFINITY ? 0.f : fast_exp2((mx - m) * alpha);
+    const float wgt = (b * QB + qlane < g.GW) ? own * __builtin_amdgcn_rcpf(l) : 0.f;
 #pragma unroll
     for (int t = 0; t < KTW; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) colacc[t][r] = __builtin_fmaf(acc[t][r], w, colacc[t][r]);
+      for (int r = 0; r < 4; ++r) colacc[t][r] = __builtin_fmaf(acc[t][r], wgt, colacc[t][r]);
+  };
+  uint2 stage2;
+  for (int b = 0; b < nblk; b += 2) {
+    block(b, stage1, stage2);
+    if (b + 1 < nblk) block(b + 1, stage2, stage1);
   }
   // column sums over the 16 query lanes of each lane group (xor within 16 lanes)
 #pragma unroll
@@ -203,6 +196,45 @@ __global__ __launch_bounds__(FTHREADS, 1) void fused_score_kernel(Geo g, const _
         if (key < g.W) out[key] = colacc[t][r];
       }
     }
+}
+
+__global__ __launch_bounds__(FTHREADS, 1) void fused_score_kernel(Geo g, const __bf16* __restrict__ q,
+                                                                   const __bf16* __restrict__ kc,
+                                                                   const int32_t* __restrict__ tables,
+                                                                   const int32_t* __restrict__ prior,
+                                                                   float* __restrict__ scores) {
+  __shared__ __align__(16) unsigned char qtile[2][QB * QLROW];
+  __shared__ __align__(16) float2 red[2][QB][FW];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int qlane = lane & 15, grp = lane >> 4;
+  const int unit = blockIdx.x;
+  const int kvh = unit % g.Hkv;
+  const int layer = (unit / g.Hkv) % g.Lyr;
+  const int n = unit / (g.Hkv * g.Lyr);
+  const int L = prior[n];
+  const int32_t* trow = tables + (long long)n * g.max_blocks;
+
+  // ---- resident keys: tile t of this wave covers window keys key0 + 16 t + (0..15)
+  const int key0 = wave * KTW * 16;
+  const unsigned char* kbytes = reinterpret_cast<const unsigned char*>(kc);
+  const PagedRows pr = paged_rows(g, trow, layer, kvh, L, 2);
+  bf16x8 kf[KTW][4];
+#pragma unroll
+  for (int t = 0; t < KTW; ++t) {
+    const int j = min(key0 + 16 * t + qlane, g.W - 1);
+    const uint4* src = reinterpret_cast<const uint4*>(kbytes + paged_row(pr, L + j) + grp * 64);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint4 v = src[s];
+      __builtin_memcpy(&kf[t][s], &v, 16);
+    }
+  }
+  // every wave of the workgroup takes the same branch (it depends on W only)
+  if (g.W >= FW * KTW * 16)
+    fused_unit<false>(g, unit, q, kf, key0, qtile, red, scores);
+  else
+    fused_unit<true>(g, unit, q, kf, key0, qtile, red, scores);
 }
 
 hipError_t launch_fused_score(const Geo& g, const void* q, const void* kc, const int32_t* tables,

@@ -15,7 +15,7 @@ import torch
 
 __all__ = [
     "KaraError", "kara_config", "make_config", "lib", "kara_check_config", "kara_workspace_bytes",
-    "kara_max_freed", "kara_score_window", "kara_select_chunks", "kara_compact_paged",
+    "kara_max_freed", "kara_score_passes", "kara_score_window", "kara_select_chunks", "kara_compact_paged",
     "kara_validate_tables", "kara_status_str", "kara_last_hip_error", "KARA_BF16", "KARA_F32",
     "EXPORTED_SYMBOLS",
 ]
@@ -23,7 +23,8 @@ __all__ = [
 KARA_BF16 = 0
 KARA_F32 = 1
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkara.so")
-EXPORTED_SYMBOLS = ("kara_check_config", "kara_workspace_bytes", "kara_max_freed", "kara_score_window",
+EXPORTED_SYMBOLS = ("kara_check_config", "kara_workspace_bytes", "kara_max_freed", "kara_score_passes",
+                    "kara_score_window",
                     "kara_select_chunks", "kara_compact_paged", "kara_validate_tables", "kara_status_str",
                     "kara_last_hip_error")
 
@@ -61,6 +62,7 @@ def lib() -> ctypes.CDLL:
             "kara_check_config": (i32, [P]),
             "kara_workspace_bytes": (sz, [P]),
             "kara_max_freed": (ctypes.c_int32, [P]),
+            "kara_score_passes": (i32, [P]),
             "kara_score_window": (i32, [P, vp, vp, vp, vp, vp, vp, sz, vp]),
             "kara_select_chunks": (i32, [P, vp, vp, vp, vp]),
             "kara_compact_paged": (i32, [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
@@ -120,6 +122,10 @@ def kara_check_config(cfg: kara_config) -> int:
 
 def kara_workspace_bytes(cfg: kara_config) -> int:
     return int(lib().kara_workspace_bytes(ctypes.byref(cfg)))
+
+
+def kara_score_passes(cfg: kara_config) -> int:
+    return int(lib().kara_score_passes(ctypes.byref(cfg)))
 
 
 def kara_max_freed(cfg: kara_config) -> int:

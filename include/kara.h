@@ -92,6 +92,12 @@ int kara_check_config(const kara_config* cfg);
  * returns 0 for an invalid cfg. */
 size_t kara_workspace_bytes(const kara_config* cfg);
 
+/* Which scorer kara_score_window runs for cfg: 1 = single pass (bf16,
+ * head_dim 128, W <= 1024: one workgroup per unit keeps the window's keys in
+ * registers), 2 = two passes (row log-sum-exp, then column mass; needs the
+ * workspace); 0 for an invalid cfg.  Both compute the same scores. */
+int kara_score_passes(const kara_config* cfg);
+
 /* Columns of freed_blocks: the most blocks one sequence can free, ceil(W/bs)+1. */
 int32_t kara_max_freed(const kara_config* cfg);
 

@@ -23,7 +23,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = K.lib()
     names = _declared()
-    assert len(names) >= 9
+    assert len(names) >= 10
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(K.EXPORTED_SYMBOLS)
@@ -72,6 +72,8 @@ def test_workspace_bytes_and_max_freed():
     assert K.kara_max_freed(c) == 1024 // 16 + 1
     assert K.kara_max_freed(_cfg(window=100, budget=90, block_size=32)) == 4 + 1
     assert K.kara_workspace_bytes(_cfg(window=0)) == 0
+    assert K.kara_score_passes(c) == 1 and K.kara_score_passes(c1) == 2 and K.kara_score_passes(c3) == 2
+    assert K.kara_score_passes(_cfg(window=0)) == 0
     assert K.kara_max_freed(_cfg(window=0)) == 0
 
 
