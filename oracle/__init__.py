@@ -5,11 +5,13 @@ leg may import this package; the product path never does.
 """
 from .kara_oracle import (  # noqa: F401
     Selection,
+    chunk_bound,
     compact_paged_sequence,
     compact_window_rows,
     compress_step,
     gather_window_rows,
     rewrite_block_table,
+    token2chunk_bridge_select,
     token2chunk_select,
     window_scores,
 )

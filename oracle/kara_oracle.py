@@ -35,6 +35,9 @@ Readings taken where the pages are silent (each is stated where used):
   [p - radius, p + radius] clipped to the window; spans are merged; the rest
   of the budget goes to the best positions outside the spans, by the same
   order; exactly ``budget`` positions are kept, listed in ascending order.
+* R20     bridging variant (not the main rule): neighbouring seeds that leave
+  at most ``gap`` positions between them are joined by keeping everything in
+  between (the explainers' "keep what lies between two important points").
 * R14-R18 compaction is in place: logical slot L + r receives the row that
   sat in slot L + kept[r]; block-table entries past the new length are freed
   in ascending logical order and set to -1; every other byte is unchanged.
@@ -148,6 +151,50 @@ def token2chunk_select(scores, budget, seeds, radius):
                      span=span, fill=np.asarray(fill, dtype=np.int64))
 
 
+def chunk_bound(seeds, radius, gap):
+    """Largest possible |U| of the bridged rule: the clipped spans cover at most
+    seeds*(2*radius+1) positions, and each of the seeds-1 bridges between
+    neighbouring seeds adds at most max(0, gap - 2*radius) positions that no
+    span covers."""
+    return seeds * (2 * radius + 1) + max(0, seeds - 1) * max(0, gap - 2 * radius)
+
+
+def token2chunk_bridge_select(scores, budget, seeds, radius, gap):
+    """Token2Chunk with bridging (variant; reading R20 of the lay explainers).
+
+    The explainers of the method ([gist-de] section "2. Das Token2Chunk-Modul",
+    and its Japanese twin) describe a chunk as everything lying between two
+    important positions, with no fixed size.  Reading taken here: take the
+    seeds and their clipped radius spans as in ``token2chunk_select``, then
+    list the seeds in ascending position; wherever two neighbouring seeds p < p'
+    leave at most ``gap`` positions between them (p' - p - 1 <= gap), every
+    position strictly between them joins U as well.  The fill and the kept list
+    follow as before.  gap = 0 adds nothing, so the rule reduces to
+    ``token2chunk_select``.  Requires 0 <= gap and
+    chunk_bound(seeds, radius, gap) <= budget <= W.
+    """
+    W = len(scores)
+    if not (0 <= seeds and 0 <= radius and 0 <= gap and chunk_bound(seeds, radius, gap) <= budget <= W):
+        raise ValueError("need chunk_bound(seeds, radius, gap) <= budget <= W and gap >= 0")
+    order = _order(scores)
+    seed_pos = order[:seeds]
+    span = np.zeros(W, dtype=bool)
+    for p in seed_pos:
+        span[max(0, p - radius):min(W - 1, p + radius) + 1] = True
+    by_pos = sorted(seed_pos)
+    for a, b in zip(by_pos[:-1], by_pos[1:]):
+        if b - a - 1 <= gap:
+            span[a:b + 1] = True
+    room = budget - int(span.sum())
+    fill = [j for j in order if not span[j]][:room]
+    keep = span.copy()
+    keep[fill] = True
+    kept = np.flatnonzero(keep).astype(np.int64)
+    assert kept.size == budget
+    return Selection(kept=kept, seeds=np.asarray(seed_pos, dtype=np.int64),
+                     span=span, fill=np.asarray(fill, dtype=np.int64))
+
+
 # --------------------------------------------------------------------------
 # a1: window addressing through a PagedAttention block table  [Kara-abs]
 # --------------------------------------------------------------------------
@@ -231,7 +278,7 @@ def rewrite_block_table(table_row, prior_len, window, budget, block_size):
 # The whole step over a batch
 # --------------------------------------------------------------------------
 def compress_step(q, k_pool, v_pool, block_tables, prior_lens, *, window, budget,
-                  seeds, radius, block_size, scores_override=None):
+                  seeds, radius, block_size, scores_override=None, gap=0):
     """Run a1-a10 for every sequence, layer and KV head.
 
     q            [S][layers][W][Hq][d]
@@ -241,6 +288,7 @@ def compress_step(q, k_pool, v_pool, block_tables, prior_lens, *, window, budget
     scores_override  optional [S][layers][Hkv][W]: select from these scores
                  instead of the oracle's own (used to pin the selection and
                  compaction stages to scores computed elsewhere).
+    gap          0: the main Token2Chunk rule; > 0: the bridging variant.
     Returns a dict with scores, kept, k_pool, v_pool, block_tables, seq_lens,
     freed (list of arrays) and num_freed.
     """
@@ -265,7 +313,11 @@ def compress_step(q, k_pool, v_pool, block_tables, prior_lens, *, window, budget
                     scores[n, layer, g] = window_scores(qg, kw)
                 else:
                     scores[n, layer, g] = np.asarray(scores_override[n, layer, g], dtype=np.float64)
-                kept[n, layer, g] = token2chunk_select(scores[n, layer, g], budget, seeds, radius).kept
+                if gap == 0:
+                    sel = token2chunk_select(scores[n, layer, g], budget, seeds, radius)
+                else:
+                    sel = token2chunk_bridge_select(scores[n, layer, g], budget, seeds, radius, gap)
+                kept[n, layer, g] = sel.kept
         compact_paged_sequence(k_out, v_out, block_tables[n], L, kept[n], block_size)
         row, fr, new_len = rewrite_block_table(block_tables[n], L, W, budget, block_size)
         tables[n] = row
