@@ -9,7 +9,7 @@ hipError_t launch_score(const Geo& g, int dtype, const void* q, const void* kc, 
                         const int32_t* prior, float* scores, float* ws, hipStream_t st);
 size_t score_workspace_bytes(const Geo& g, int dtype);
 bool fused_score_supported(const Geo& g, int dtype);
-hipError_t launch_select(const Geo& g, const float* scores, int32_t* kept, uint8_t* mask, hipStream_t st);
+hipError_t launch_select(const Geo& g, int gap, const float* scores, int32_t* kept, uint8_t* mask, hipStream_t st);
 hipError_t launch_compact(const Geo& g, int dtype, void* kc, void* vc, int32_t* tables, const int32_t* prior,
                           int32_t* seq_lens, const int32_t* kept, int32_t* freed, int32_t* num_freed,
                           int max_freed, hipStream_t st);
@@ -114,7 +114,23 @@ int kara_select_chunks(const kara_config* cfg, const float* scores, int32_t* kep
   if (s) return s;
   if (cfg->num_seqs == 0) return KARA_OK;
   if (!scores || !kept) return KARA_ENULL;
-  return hip_status(kara::launch_select(geo(cfg), scores, kept, mask, (hipStream_t)stream));
+  return hip_status(kara::launch_select(geo(cfg), 0, scores, kept, mask, (hipStream_t)stream));
+}
+
+int64_t kara_chunk_bound(const kara_config* cfg, int32_t gap) {
+  if (!cfg || cfg->seeds < 0 || cfg->radius < 0 || gap < 0) return -1;
+  const int64_t s = cfg->seeds, r = cfg->radius, extra = (int64_t)gap - 2 * r;
+  return s * (2 * r + 1) + (s > 1 ? s - 1 : 0) * (extra > 0 ? extra : 0);
+}
+
+int kara_select_chunks_bridged(const kara_config* cfg, int32_t gap, const float* scores, int32_t* kept,
+                               uint8_t* mask, void* stream) {
+  int s = check(cfg);
+  if (s) return s;
+  if (gap < 0 || gap > cfg->window || kara_chunk_bound(cfg, gap) > cfg->budget) return KARA_EINVAL;
+  if (cfg->num_seqs == 0) return KARA_OK;
+  if (!scores || !kept) return KARA_ENULL;
+  return hip_status(kara::launch_select(geo(cfg), gap, scores, kept, mask, (hipStream_t)stream));
 }
 
 int kara_compact_paged(const kara_config* cfg, void* k_cache, void* v_cache, int32_t* block_tables,

@@ -18,7 +18,7 @@ namespace kara {
 
 constexpr int SEL_THREADS = 256;
 constexpr int SEL_WAVES = SEL_THREADS / 64;
-constexpr uint8_t IN_SPAN = 1, KEEP = 2;
+constexpr uint8_t IN_SPAN = 1, KEEP = 2, SEED = 4;
 
 // float -> uint32 whose unsigned order is the float order (-0 == +0).
 __device__ inline uint32_t order_key(float f) {
@@ -115,7 +115,9 @@ __device__ inline void mark_top(const uint32_t* keys, uint8_t* flags, uint8_t em
   *nmarked = cnt;
 }
 
-__global__ __launch_bounds__(SEL_THREADS) void select_kernel(Geo g, const float* __restrict__ scores,
+// gap > 0 selects the bridging variant: neighbouring seeds (by position) that
+// leave at most `gap` positions between them also keep everything in between.
+__global__ __launch_bounds__(SEL_THREADS) void select_kernel(Geo g, int gap, const float* __restrict__ scores,
                                                              int32_t* __restrict__ kept,
                                                              uint8_t* __restrict__ mask) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -147,6 +149,22 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(Geo g, const float*
       for (int x = lo; x <= hi; ++x) flags[x] = IN_SPAN;   // concurrent writers store the same value
     }
     __syncthreads();
+    if (gap > 0 && g.seeds > 1) {
+      for (int a = 0; a < ns; ++a) flags[seeds_mine[a]] = IN_SPAN | SEED;
+      __syncthreads();
+      // The owner of seed p looks for the next seed p' within gap + 1 positions;
+      // the positions strictly between belong to this pair alone, so each is
+      // written by exactly one thread.
+      for (int a = 0; a < ns; ++a) {
+        const int p = seeds_mine[a];
+        const int lim = min(W - 1, p + gap + 1);
+        int nxt = -1;
+        for (int x = p + 1; x <= lim; ++x)
+          if (flags[x] & SEED) { nxt = x; break; }
+        for (int x = p + 1; x < nxt; ++x) flags[x] |= IN_SPAN;
+      }
+      __syncthreads();
+    }
   }
   // |U|
   const int j0 = t * E, j1 = min(W, j0 + E);
@@ -175,11 +193,12 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(Geo g, const float*
   }
 }
 
-hipError_t launch_select(const Geo& g, const float* scores, int32_t* kept, uint8_t* mask, hipStream_t st) {
+hipError_t launch_select(const Geo& g, int gap, const float* scores, int32_t* kept, uint8_t* mask,
+                         hipStream_t st) {
   const long long units = (long long)g.S * g.Lyr * g.Hkv;
   if (units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const size_t lds = sizeof(SelScratch) + (size_t)g.W * 4 + (size_t)g.W;
-  hipLaunchKernelGGL(select_kernel, dim3((unsigned)units), dim3(SEL_THREADS), lds, st, g, scores, kept, mask);
+  hipLaunchKernelGGL(select_kernel, dim3((unsigned)units), dim3(SEL_THREADS), lds, st, g, gap, scores, kept, mask);
   return hipGetLastError();
 }
 

@@ -15,7 +15,8 @@ import torch
 
 __all__ = [
     "KaraError", "kara_config", "make_config", "lib", "kara_check_config", "kara_workspace_bytes",
-    "kara_max_freed", "kara_score_passes", "kara_score_window", "kara_select_chunks", "kara_compact_paged",
+    "kara_max_freed", "kara_score_passes", "kara_score_window", "kara_select_chunks", "kara_chunk_bound",
+    "kara_select_chunks_bridged", "kara_compact_paged",
     "kara_validate_tables", "kara_status_str", "kara_last_hip_error", "KARA_BF16", "KARA_F32",
     "EXPORTED_SYMBOLS",
 ]
@@ -25,7 +26,8 @@ KARA_F32 = 1
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkara.so")
 EXPORTED_SYMBOLS = ("kara_check_config", "kara_workspace_bytes", "kara_max_freed", "kara_score_passes",
                     "kara_score_window",
-                    "kara_select_chunks", "kara_compact_paged", "kara_validate_tables", "kara_status_str",
+                    "kara_select_chunks", "kara_chunk_bound", "kara_select_chunks_bridged",
+                    "kara_compact_paged", "kara_validate_tables", "kara_status_str",
                     "kara_last_hip_error")
 
 
@@ -65,6 +67,8 @@ def lib() -> ctypes.CDLL:
             "kara_score_passes": (i32, [P]),
             "kara_score_window": (i32, [P, vp, vp, vp, vp, vp, vp, sz, vp]),
             "kara_select_chunks": (i32, [P, vp, vp, vp, vp]),
+            "kara_chunk_bound": (ctypes.c_int64, [P, ctypes.c_int32]),
+            "kara_select_chunks_bridged": (i32, [P, ctypes.c_int32, vp, vp, vp, vp]),
             "kara_compact_paged": (i32, [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
             "kara_validate_tables": (i32, [P, vp, vp, vp, vp]),
             "kara_status_str": (ctypes.c_char_p, [i32]),
@@ -164,6 +168,20 @@ def kara_select_chunks(cfg, scores, kept, mask=None, stream=None):
         _need(mask, "mask", torch.uint8, (S, Lyr, Hkv, W))
     _check(lib().kara_select_chunks(ctypes.byref(cfg), _ptr(scores), _ptr(kept), _ptr(mask), _stream(stream)),
            "kara_select_chunks")
+
+
+def kara_chunk_bound(cfg: kara_config, gap: int) -> int:
+    return int(lib().kara_chunk_bound(ctypes.byref(cfg), int(gap)))
+
+
+def kara_select_chunks_bridged(cfg, gap, scores, kept, mask=None, stream=None):
+    S, Lyr, Hkv, W, B = cfg.num_seqs, cfg.num_layers, cfg.num_kv_heads, cfg.window, cfg.budget
+    _need(scores, "scores", torch.float32, (S, Lyr, Hkv, W))
+    _need(kept, "kept", torch.int32, (S, Lyr, Hkv, B))
+    if mask is not None:
+        _need(mask, "mask", torch.uint8, (S, Lyr, Hkv, W))
+    _check(lib().kara_select_chunks_bridged(ctypes.byref(cfg), int(gap), _ptr(scores), _ptr(kept), _ptr(mask),
+                                            _stream(stream)), "kara_select_chunks_bridged")
 
 
 def kara_compact_paged(cfg, k_cache, v_cache, block_tables, prior_lens, seq_lens, kept, freed_blocks, num_freed,

@@ -126,6 +126,27 @@ int kara_select_chunks(const kara_config* cfg, const float* scores, int32_t* kep
                        void* stream);
 
 /*
+ * Largest number of positions the chunks of the bridging rule below can cover:
+ * seeds*(2*radius+1) + max(0, seeds-1) * max(0, gap - 2*radius).  -1 if cfg is
+ * NULL or seeds, radius or gap is negative.  Host only.
+ */
+int64_t kara_chunk_bound(const kara_config* cfg, int32_t gap);
+
+/*
+ * Step 2, bridging variant of Token2Chunk (the method's lay explainers,
+ * gist.science, section "2. Das Token2Chunk-Modul": a chunk is whatever lies
+ * between two important positions and has no fixed size).  Same as
+ * kara_select_chunks, except that after the radius spans are formed the seeds
+ * are taken in ascending position, and two neighbouring seeds p < p' with
+ * p' - p - 1 <= gap also keep every position between them.  gap = 0 gives
+ * exactly kara_select_chunks.  Requires 0 <= gap <= window and
+ * kara_chunk_bound(cfg, gap) <= budget, else KARA_EINVAL.  Same layouts,
+ * ownership and errors as kara_select_chunks.
+ */
+int kara_select_chunks_bridged(const kara_config* cfg, int32_t gap, const float* scores, int32_t* kept,
+                               uint8_t* mask, void* stream);
+
+/*
  * Step 3 - in-place compaction into PagedAttention blocks (Kara abstract: the
  * method is adapted to PagedAttention and lowers KV memory).  For every unit
  * and r < budget, the K and V rows of logical slot L+r become the old rows of

@@ -52,11 +52,17 @@ class Outputs:
         return True
 
 
-def run_step(wl: Workload, cfg=None, out: Outputs | None = None, with_mask=True, stream=None):
+def run_step(wl: Workload, cfg=None, out: Outputs | None = None, with_mask=True, stream=None, gap=None):
+    """Score, select and compact through the C ABI; gap selects the bridging
+    variant of the selection (None: the main rule)."""
     cfg = cfg or config_of(wl)
     out = out or Outputs(cfg, wl.q.device)
     K.kara_score_window(cfg, wl.q, wl.k_pool, wl.block_tables, wl.prior_lens, out["scores"], out.ws, stream)
-    K.kara_select_chunks(cfg, out["scores"], out["kept"], out["mask"] if with_mask else None, stream)
+    mask = out["mask"] if with_mask else None
+    if gap is None:
+        K.kara_select_chunks(cfg, out["scores"], out["kept"], mask, stream)
+    else:
+        K.kara_select_chunks_bridged(cfg, gap, out["scores"], out["kept"], mask, stream)
     K.kara_compact_paged(cfg, wl.k_pool, wl.v_pool, wl.block_tables, wl.prior_lens, out["seq_lens"], out["kept"],
                          out["freed"], out["num_freed"], stream)
     torch.cuda.synchronize()

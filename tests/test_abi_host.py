@@ -107,3 +107,19 @@ def test_status_strings():
     for code in (0, -1, -2, -3, -4, -5, 99):
         assert isinstance(K.kara_status_str(code), str) and K.kara_status_str(code)
     assert K.kara_last_hip_error() == 0
+
+
+def test_chunk_bound_matches_the_union_bound():
+    import oracle
+    for s, r, gap in [(0, 0, 0), (1, 3, 50), (3, 1, 1), (3, 1, 2), (3, 1, 7), (24, 8, 40), (12, 7, 0)]:
+        assert K.kara_chunk_bound(_cfg(seeds=s, radius=r), gap) == oracle.chunk_bound(s, r, gap)
+    assert K.kara_chunk_bound(_cfg(), -1) == -1
+
+
+def test_bridged_select_rejects_bad_gap_before_device_work():
+    L = K.lib()
+    c = _cfg(window=64, budget=20, seeds=3, radius=1)            # spans 9, bridges add <= 2*(gap-2)
+    assert L.kara_select_chunks_bridged(ctypes.byref(c), -1, None, None, None, None) == -1
+    assert L.kara_select_chunks_bridged(ctypes.byref(c), 65, None, None, None, None) == -1
+    assert L.kara_select_chunks_bridged(ctypes.byref(c), 8, None, None, None, None) == -1    # 9 + 12 > 20
+    assert L.kara_select_chunks_bridged(ctypes.byref(c), 7, None, None, None, None) == -2    # 9 + 10 <= 20

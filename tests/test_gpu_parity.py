@@ -153,3 +153,56 @@ def test_host_rejects_bad_arguments_before_enqueueing():
     torch.cuda.synchronize()
     assert out.guards_intact()
     assert torch.isnan(out["scores"]).all()
+
+
+BRIDGED = [
+    (SMALL[1], 16),                                  # bound 15 + 2 * 12 = 39 <= 40
+    (SMALL[2], 40),                                  # its two seeds lie 79 apart: no bridge forms
+    (SMALL[5], 40),                                  # one seed: nothing to bridge, gap = window
+    (SMALL[8], 29),                                  # bound exactly the budget
+    (KaraShape("bridge_wide", 111, num_seqs=2, num_layers=2, num_q_heads=8, num_kv_heads=2, head_dim=128,
+               window=256, budget=200, seeds=4, radius=1, prior=("uniform", 0, 40), plants=True), 64),
+    (KaraShape("bridge_wide_f32", 112, num_seqs=1, num_layers=1, num_q_heads=4, num_kv_heads=2, head_dim=64,
+               window=96, budget=90, seeds=6, radius=0, prior=("fixed", 9), dtype="f32"), 16),
+]
+
+
+@pytest.mark.parametrize("shape,gap", BRIDGED, ids=lambda x: getattr(x, "name", str(x)))
+def test_bridged_selection_full_parity(shape, gap):
+    from decode_kv_cache_amd import kara as K
+    s = shape
+    wl = make_workload(s, "cuda")
+    k0, v0 = bits(wl.k_pool), bits(wl.v_pool)
+    cfg, out = run_step(wl, gap=gap)
+    assert out.guards_intact()
+    c_gpu = out["scores"].cpu().numpy()
+    kept = out["kept"].cpu().numpy()
+    mask = out["mask"].cpu().numpy()
+    bridged = 0
+    for n in range(s.num_seqs):
+        for layer in range(s.num_layers):
+            for g in range(s.num_kv_heads):
+                c = c_gpu[n, layer, g].astype(np.float64)
+                sel = oracle.token2chunk_bridge_select(c, s.budget, s.seeds, s.radius, gap)
+                assert kept[n, layer, g].tolist() == sel.kept.tolist(), (s.name, n, layer, g)
+                assert np.array_equal(np.flatnonzero(mask[n, layer, g]), sel.kept)
+                plain = oracle.token2chunk_select(c, s.budget, s.seeds, s.radius)
+                bridged += int(sel.span.sum() - plain.span.sum())
+    if s.name not in ("gqa7_plants", "bs1"):
+        assert bridged > 0, "no unit exercised a bridge"
+    ref = oracle.compress_step(np.zeros((s.num_seqs, s.num_layers, s.window, s.num_q_heads, 1)), k0, v0,
+                               wl.host_tables, wl.host_prior_lens, window=s.window, budget=s.budget, seeds=s.seeds,
+                               radius=s.radius, block_size=s.block_size, scores_override=c_gpu, gap=gap)
+    assert np.array_equal(ref["kept"], kept)
+    assert np.array_equal(bits(wl.k_pool), ref["k_pool"])
+    assert np.array_equal(bits(wl.v_pool), ref["v_pool"])
+    assert np.array_equal(wl.block_tables.cpu().numpy(), ref["block_tables"])
+    assert np.array_equal(out["seq_lens"].cpu().numpy(), ref["seq_lens"])
+    # gap 0 of the bridged call is the main rule, bit for bit
+    kept0 = torch.empty_like(out["kept"])
+    kept1 = torch.empty_like(out["kept"])
+    K.kara_select_chunks_bridged(cfg, 0, out["scores"], kept0)
+    K.kara_select_chunks(cfg, out["scores"], kept1)
+    torch.cuda.synchronize()
+    assert torch.equal(kept0, kept1)
+    print(f"{s.name}: gap {gap}, {bridged} bridged positions", flush=True)
