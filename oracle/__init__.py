@@ -10,6 +10,7 @@ from .kara_oracle import (  # noqa: F401
     compact_window_rows,
     compress_step,
     gather_window_rows,
+    paged_decode_attention,
     rewrite_block_table,
     token2chunk_bridge_select,
     token2chunk_select,

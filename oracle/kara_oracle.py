@@ -38,6 +38,9 @@ Readings taken where the pages are silent (each is stated where used):
 * R20     bridging variant (not the main rule): neighbouring seeds that leave
   at most ``gap`` positions between them are joined by keeping everything in
   between (the explainers' "keep what lies between two important points").
+* R21/R22 the consumer (decode attention) reads every cached slot [0, seq_len)
+  of the sequence through its block table, scale 1/sqrt(d), GQA as in R4; an
+  empty cache yields a zero output.
 * R14-R18 compaction is in place: logical slot L + r receives the row that
   sat in slot L + kept[r]; block-table entries past the new length are freed
   in ascending logical order and set to -1; every other byte is unchanged.
@@ -272,6 +275,47 @@ def rewrite_block_table(table_row, prior_len, window, budget, block_size):
     freed = row[nb_new:nb_old].copy()
     row[nb_new:nb_old] = -1
     return row, freed, prior_len + budget
+
+
+# --------------------------------------------------------------------------
+# Consumer: one decode step of paged attention over the (compacted) cache
+# --------------------------------------------------------------------------
+def paged_decode_attention(q_dec, k_pool, v_pool, block_tables, seq_lens, block_size):
+    """Attention of one new query per head over a sequence's cached slots.
+
+    The Kara abstract ([Kara-abs]) places the compressed cache inside a
+    PagedAttention store and claims lower KV memory and higher output
+    throughput; the decode step that reads the cache is ordinary scaled
+    dot-product attention over the logical slots [0, seq_len) reached through
+    the block table (reading R21: the query attends every cached slot, no
+    mask inside the cache; query head h reads KV head h // G as in R4).
+
+    q_dec        [S][layers][Hq][d]
+    k_pool/v_pool [layers][num_blocks][Hkv][block_size][d]
+    block_tables [S][max_blocks];  seq_lens [S]
+    Returns o [S][layers][Hq][d] in fp64:
+        o = sum_j softmax_j(q . k_j / sqrt(d)) v_j ;  seq_len 0 gives o = 0
+    (reading R22: an empty cache contributes nothing).
+    """
+    S, layers, Hq, d = q_dec.shape
+    Hkv = k_pool.shape[2]
+    G = Hq // Hkv
+    out = np.zeros((S, layers, Hq, d), dtype=np.float64)
+    for n in range(S):
+        T = int(seq_lens[n])
+        if T == 0:
+            continue
+        for layer in range(layers):
+            for g in range(Hkv):
+                K = gather_window_rows(k_pool, block_tables[n], layer, g, 0, T, block_size).astype(np.float64)
+                V = gather_window_rows(v_pool, block_tables[n], layer, g, 0, T, block_size).astype(np.float64)
+                for h in range(g * G, (g + 1) * G):
+                    logits = K @ np.asarray(q_dec[n, layer, h], dtype=np.float64) / np.sqrt(d)
+                    logits -= logits.max()
+                    p = np.exp(logits)
+                    p /= p.sum()
+                    out[n, layer, h] = p @ V
+    return out
 
 
 # --------------------------------------------------------------------------
