@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkara.so")
-SOURCES = ["api.hip", "score.hip", "score_fused.hip", "select.hip", "compact.hip"]
+SOURCES = ["api.hip", "score.hip", "score_fused.hip", "select.hip", "compact.hip", "decode_attn.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

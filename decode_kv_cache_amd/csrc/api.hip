@@ -15,6 +15,10 @@ hipError_t launch_compact(const Geo& g, int dtype, void* kc, void* vc, int32_t* 
                           int max_freed, hipStream_t st);
 hipError_t launch_validate(const Geo& g, const int32_t* tables, const int32_t* prior, int32_t* bad,
                            hipStream_t st);
+size_t decode_attn_workspace_bytes(const Geo& g);
+int decode_attn_splits(const Geo& g);
+hipError_t launch_decode_attn(const Geo& g, int dtype, const void* q, const void* kc, const void* vc,
+                              const int32_t* tables, const int32_t* lens, float* out, float* ws, hipStream_t st);
 }  // namespace kara
 
 namespace {
@@ -131,6 +135,30 @@ int kara_select_chunks_bridged(const kara_config* cfg, int32_t gap, const float*
   if (cfg->num_seqs == 0) return KARA_OK;
   if (!scores || !kept) return KARA_ENULL;
   return hip_status(kara::launch_select(geo(cfg), gap, scores, kept, mask, (hipStream_t)stream));
+}
+
+size_t kara_decode_attention_workspace_bytes(const kara_config* cfg) {
+  if (check(cfg) != KARA_OK) return 0;
+  return kara::decode_attn_workspace_bytes(geo(cfg));
+}
+
+int kara_decode_attention_splits(const kara_config* cfg) {
+  if (check(cfg) != KARA_OK) return 0;
+  return kara::decode_attn_splits(geo(cfg));
+}
+
+int kara_decode_attention(const kara_config* cfg, const void* q_dec, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* seq_lens, float* out, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  int s = check(cfg);
+  if (s) return s;
+  if (cfg->num_seqs == 0) return KARA_OK;
+  if (!q_dec || !k_cache || !v_cache || !block_tables || !seq_lens || !out) return KARA_ENULL;
+  const kara::Geo g = geo(cfg);
+  const size_t need = kara::decode_attn_workspace_bytes(g);
+  if (need && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255))) return KARA_EWORKSPACE;
+  return hip_status(kara::launch_decode_attn(g, cfg->dtype, q_dec, k_cache, v_cache, block_tables, seq_lens, out,
+                                             (float*)workspace, (hipStream_t)stream));
 }
 
 int kara_compact_paged(const kara_config* cfg, void* k_cache, void* v_cache, int32_t* block_tables,

@@ -16,7 +16,8 @@ import torch
 __all__ = [
     "KaraError", "kara_config", "make_config", "lib", "kara_check_config", "kara_workspace_bytes",
     "kara_max_freed", "kara_score_passes", "kara_score_window", "kara_select_chunks", "kara_chunk_bound",
-    "kara_select_chunks_bridged", "kara_compact_paged",
+    "kara_select_chunks_bridged", "kara_compact_paged", "kara_decode_attention", "kara_decode_attention_splits",
+    "kara_decode_attention_workspace_bytes",
     "kara_validate_tables", "kara_status_str", "kara_last_hip_error", "KARA_BF16", "KARA_F32",
     "EXPORTED_SYMBOLS",
 ]
@@ -27,7 +28,8 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkara.so
 EXPORTED_SYMBOLS = ("kara_check_config", "kara_workspace_bytes", "kara_max_freed", "kara_score_passes",
                     "kara_score_window",
                     "kara_select_chunks", "kara_chunk_bound", "kara_select_chunks_bridged",
-                    "kara_compact_paged", "kara_validate_tables", "kara_status_str",
+                    "kara_compact_paged", "kara_decode_attention_workspace_bytes", "kara_decode_attention_splits",
+                    "kara_decode_attention", "kara_validate_tables", "kara_status_str",
                     "kara_last_hip_error")
 
 
@@ -71,6 +73,9 @@ def lib() -> ctypes.CDLL:
             "kara_select_chunks_bridged": (i32, [P, ctypes.c_int32, vp, vp, vp, vp]),
             "kara_compact_paged": (i32, [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
             "kara_validate_tables": (i32, [P, vp, vp, vp, vp]),
+            "kara_decode_attention_workspace_bytes": (sz, [P]),
+            "kara_decode_attention_splits": (i32, [P]),
+            "kara_decode_attention": (i32, [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "kara_status_str": (ctypes.c_char_p, [i32]),
             "kara_last_hip_error": (i32, []),
         }
@@ -198,6 +203,28 @@ def kara_compact_paged(cfg, k_cache, v_cache, block_tables, prior_lens, seq_lens
     _check(lib().kara_compact_paged(ctypes.byref(cfg), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                     _ptr(prior_lens), _ptr(seq_lens), _ptr(kept), _ptr(freed_blocks),
                                     _ptr(num_freed), _stream(stream)), "kara_compact_paged")
+
+
+def kara_decode_attention_workspace_bytes(cfg: kara_config) -> int:
+    return int(lib().kara_decode_attention_workspace_bytes(ctypes.byref(cfg)))
+
+
+def kara_decode_attention_splits(cfg: kara_config) -> int:
+    return int(lib().kara_decode_attention_splits(ctypes.byref(cfg)))
+
+
+def kara_decode_attention(cfg, q_dec, k_cache, v_cache, block_tables, seq_lens, out, workspace=None, stream=None):
+    S, Lyr, Hq, d = cfg.num_seqs, cfg.num_layers, cfg.num_q_heads, cfg.head_dim
+    _need(q_dec, "q_dec", _elem(cfg), (S, Lyr, Hq, d))
+    _need(k_cache, "k_cache", _elem(cfg), _pool_shape(cfg))
+    _need(v_cache, "v_cache", _elem(cfg), _pool_shape(cfg))
+    _need(block_tables, "block_tables", torch.int32, (S, cfg.max_blocks_per_seq))
+    _need(seq_lens, "seq_lens", torch.int32, (S,))
+    _need(out, "out", torch.float32, (S, Lyr, Hq, d))
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().kara_decode_attention(ctypes.byref(cfg), _ptr(q_dec), _ptr(k_cache), _ptr(v_cache),
+                                       _ptr(block_tables), _ptr(seq_lens), _ptr(out), _ptr(workspace), nbytes,
+                                       _stream(stream)), "kara_decode_attention")
 
 
 def kara_validate_tables(cfg, block_tables, prior_lens, bad_seqs, stream=None):

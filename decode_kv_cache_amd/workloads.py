@@ -25,7 +25,10 @@ reasoning-model decode workloads the Kara pages describe):
   ids; the pool holds exactly the blocks every sequence needs for L + W
   tokens.  The window slots and the prior-context slots that share the
   window's first block are random data; every other slot holds a canary
-  value so that stray writes show up.
+  value so that stray writes show up;
+* for the decode-attention consumer, ``fill_prior_context`` overwrites the
+  remaining prior slots [0, L - L % bs) with i.i.d. N(0, 1) keys and values,
+  and ``decode_queries`` draws one N(0, 1) query per (sequence, layer, head).
 
 Seeds are derived from (shape id, sequence, layer, tensor tag) with numpy's
 SeedSequence; torch generators on the target device draw the bulk values,
@@ -40,8 +43,8 @@ from dataclasses import dataclass, field, replace
 import numpy as np
 import torch
 
-__all__ = ["KaraShape", "SHAPES", "shape_by_name", "Workload", "make_workload",
-           "CANARY_BF16_BITS", "CANARY_F32"]
+__all__ = ["KaraShape", "SHAPES", "shape_by_name", "Workload", "make_workload", "fill_prior_context",
+           "decode_queries", "CANARY_BF16_BITS", "CANARY_F32"]
 
 # Canary for pool slots the step must never touch (a normal bf16 value that
 # random data essentially never produces exactly: -0.013916015625).
@@ -130,6 +133,7 @@ def _torch_gen(device, *key) -> torch.Generator:
 
 
 _TAG_Q, _TAG_K, _TAG_V, _TAG_U, _TAG_HEAD_K, _TAG_HEAD_V = 11, 12, 13, 14, 15, 16
+_TAG_PRIOR_K, _TAG_PRIOR_V, _TAG_QDEC = 17, 18, 19
 
 
 @dataclass
@@ -284,3 +288,37 @@ def make_workload(shape: KaraShape, device="cpu", *, canary=True) -> Workload:
                     prior_lens=torch.from_numpy(prior.astype(np.int32)).to(device),
                     num_blocks=num_blocks, max_blocks=max_blocks,
                     host_prior_lens=prior, host_tables=tables)
+
+
+def fill_prior_context(wl: Workload) -> None:
+    """Fill the prior slots [0, L - L % bs) of every sequence with seeded
+    N(0, 1) keys and values (the head block's prior slots already hold random
+    data), so that attention over the whole cache sees no canary rows."""
+    s = wl.shape
+    bs, Hkv, d = s.block_size, s.num_kv_heads, s.head_dim
+    dev = wl.k_pool.device
+    for n in range(s.num_seqs):
+        L = int(wl.host_prior_lens[n])
+        full = L - L % bs
+        if full == 0:
+            continue
+        p = np.arange(full)
+        blk = torch.from_numpy(wl.host_tables[n, p // bs].astype(np.int64)).to(dev)
+        off = torch.from_numpy((p % bs).astype(np.int64)).to(dev)
+        for l in range(s.num_layers):
+            pk = torch.randn((full, Hkv, d), generator=_torch_gen(dev, s.shape_id, n, l, _TAG_PRIOR_K),
+                             device=dev, dtype=torch.float32)
+            pv = torch.randn((full, Hkv, d), generator=_torch_gen(dev, s.shape_id, n, l, _TAG_PRIOR_V),
+                             device=dev, dtype=torch.float32)
+            wl.k_pool[l][blk, :, off, :] = pk.to(wl.k_pool.dtype)
+            wl.v_pool[l][blk, :, off, :] = pv.to(wl.v_pool.dtype)
+
+
+def decode_queries(shape: KaraShape, device="cpu") -> torch.Tensor:
+    """One seeded N(0, 1) decode query per (sequence, layer, query head):
+    [S][layers][Hq][d] in the shape's dtype."""
+    tdtype = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+    g = _torch_gen(device, shape.shape_id, 0, 0, _TAG_QDEC)
+    q = torch.randn((shape.num_seqs, shape.num_layers, shape.num_q_heads, shape.head_dim), generator=g,
+                    device=device, dtype=torch.float32)
+    return q.to(tdtype)

@@ -16,8 +16,8 @@
  *                           kept = ascending list of exactly `budget` window positions
  *   3. kara_compact_paged : slot L+r <- slot L+kept[r] (K and V, in place), then every
  *                           sequence's block table drops the blocks past L+budget.
- * The score, the Token2Chunk rule and the in-place layout are the readings this
- * library records where the pages give no formula (see the design notes).
+ * The pages give no formula for the score, the Token2Chunk rule or the in-place
+ * layout; the definitions above are the plainest readings of their text.
  *
  * Conventions for every entry point
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library
@@ -161,6 +161,35 @@ int kara_select_chunks_bridged(const kara_config* cfg, int32_t gap, const float*
 int kara_compact_paged(const kara_config* cfg, void* k_cache, void* v_cache, int32_t* block_tables,
                        const int32_t* prior_lens, int32_t* seq_lens, const int32_t* kept,
                        int32_t* freed_blocks, int32_t* num_freed, void* stream);
+
+/*
+ * Consumer of the compacted cache: one decode step of paged attention (Kara
+ * abstract: the compressed window lives in a PagedAttention store whose
+ * smaller footprint raises output throughput).  For every sequence n, layer
+ * and query head h (KV head h / (num_q_heads / num_kv_heads)):
+ *   out[n][l][h] = sum_{j < T} softmax_j(q_dec[n][l][h] . k_j / sqrt(head_dim)) v_j
+ * over the logical slots j < T = seq_lens[n] of the sequence, read through its
+ * block table (after kara_compact_paged, T = L + budget).  T = 0 gives zeros;
+ * T is clamped to max_blocks_per_seq * block_size.
+ *   q_dec  [num_seqs][num_layers][num_q_heads][head_dim], cfg.dtype
+ *   out    float [num_seqs][num_layers][num_q_heads][head_dim]
+ *   k_cache, v_cache, block_tables: as above; seq_lens int32 [num_seqs]
+ * Only the fields num_seqs, num_layers, num_q_heads, num_kv_heads, head_dim,
+ * block_size, dtype, max_blocks_per_seq and num_blocks matter, but the whole
+ * configuration must be valid.  workspace: device memory of at least
+ * kara_decode_attention_workspace_bytes(cfg) bytes, 256-byte aligned (may be
+ * NULL when that is 0); it holds per-split partial results.  Errors:
+ * KARA_EINVAL, KARA_ENULL, KARA_EWORKSPACE, KARA_EHIP.
+ */
+size_t kara_decode_attention_workspace_bytes(const kara_config* cfg);
+
+/* Number of workgroups that share one (sequence, layer, head group) slot range
+ * in kara_decode_attention (1 = no merge pass); 0 for an invalid cfg. */
+int kara_decode_attention_splits(const kara_config* cfg);
+
+int kara_decode_attention(const kara_config* cfg, const void* q_dec, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* seq_lens, float* out, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /*
  * Debug check of the device-side addressing data: for every sequence, L >= 0,
