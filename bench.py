@@ -6,6 +6,11 @@ every (sequence, layer, KV head) of the workload, inputs resident in HBM.
 Between steps the window blocks and block tables are restored from a
 pristine copy (outside the timed events; compaction is in place).
 
+After the timed steps, the consumer of the cache (one decode step of paged
+attention, kara_decode_attention) is timed over the compacted cache (L + B
+slots per sequence) and over the same cache before compaction (L + W slots),
+and reported with its HBM roofline beside the step.
+
 Prints ONE JSON line: metric, value (window tokens per second), per-stage
 times, the roofline of the dominant kernel, and the fp64 CPU oracle timed on
 a bounded sample of the same workload.
@@ -13,7 +18,6 @@ a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -40,16 +44,14 @@ def parse():
     p.add_argument("--workload", default="llama8b_b64")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--consumer-reps", type=int, default=10,
+                   help="timed decode-attention passes over the cache before and after compaction (0: skip)")
     return p.parse_args()
 
 
 def kernel_source_hash():
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "decode_kv_cache_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
-    return h.hexdigest()[:16]
+    from decode_kv_cache_amd.profiling import kernel_source_hash as h
+    return h()
 
 
 def measured_traffic(workload, kernel_hash):
@@ -231,6 +233,45 @@ def main():
                     "frac": round(cbytes / t_c / 1e9 / PEAK_HBM_GBS, 4),
                     "algorithmic": f"4*B*d*elem = {4 * B * d * shape.elem_bytes} B per unit x {shape.units} units"}
 
+    consumer = None
+    if a.consumer_reps > 0:
+        from decode_kv_cache_amd.workloads import decode_queries
+        q_dec = decode_queries(shape, dev)
+        att = torch.empty((S, Lyr, shape.num_q_heads, d), dtype=torch.float32, device=dev)
+        aws = torch.empty(K.kara_decode_attention_workspace_bytes(cfg) // 4 + 64, dtype=torch.float32, device=dev)
+
+        def attend_ms(lens):
+            for _ in range(2):
+                K.kara_decode_attention(cfg, q_dec, wl.k_pool, wl.v_pool, wl.block_tables, lens, att, aws, st)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(st)
+            for _ in range(a.consumer_reps):
+                K.kara_decode_attention(cfg, q_dec, wl.k_pool, wl.v_pool, wl.block_tables, lens, att, aws, st)
+            ev[1].record(st)
+            torch.cuda.synchronize()
+            return ev[0].elapsed_time(ev[1]) / a.consumer_reps
+
+        kv_row = Lyr * Hkv * d * shape.elem_bytes * 2          # K and V bytes per slot over all layers
+        res = {}
+        for tag, lens in (("compacted", seq_lens), ("full", None)):
+            if lens is None:
+                restore()
+                torch.cuda.synchronize()
+                lens = (wl.prior_lens + W).to(torch.int32)
+            n_slots = int(lens.sum().item())
+            t_ms = attend_ms(lens)
+            res[tag] = (t_ms, n_slots * kv_row)
+        (tc, bc), (tf, bf) = res["compacted"], res["full"]
+        consumer = {"call": "kara_decode_attention (one decode step, every sequence, layer and query head)",
+                    "ms_compacted": round(tc, 4), "ms_full": round(tf, 4), "speedup": round(tf / tc, 4),
+                    "kv_bytes_compacted": bc, "kv_bytes_full": bf,
+                    "roofline": {"bound": "hbm", "achieved": round(bc / tc / 1e6, 1), "peak": PEAK_HBM_GBS,
+                                 "unit": "GB/s", "frac": round(bc / tc / 1e6 / PEAK_HBM_GBS, 4),
+                                 "algorithmic": "2 * seq_len * num_layers * num_kv_heads * head_dim * elem bytes "
+                                                "(each cached K and V row read once)"},
+                    "splits": K.kara_decode_attention_splits(cfg)}
+        log(f"[bench] decode attention: compacted {tc:.3f} ms ({bc / tc / 1e6:.0f} GB/s), full {tf:.3f} ms")
+
     cpu = None
     if not a.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on a CPU sample")
@@ -249,6 +290,7 @@ def main():
                       "compact": round(float(np.mean(t_cmp)), 4)},
         "roofline": roof,
         "compact_roofline": compact_roof,
+        "decode_attention": consumer,
         "cpu_baseline": cpu,
         "kernel_hash": khash,
         "wall_ms_per_step_incl_restore": round(wall / a.steps * 1e3, 3),

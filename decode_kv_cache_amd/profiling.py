@@ -1,0 +1,150 @@
+"""Helpers for the rocprofv3 measurements of the Kara kernels.
+
+    python -m decode_kv_cache_amd.profiling copy --mib 2048
+        a plain device copy of a known size (an elementwise torch kernel that
+        reads and writes every byte once), run under ``rocprofv3 --pmc`` to
+        calibrate FETCH_SIZE / WRITE_SIZE against bytes actually moved;
+    python -m decode_kv_cache_amd.profiling stats <rocprofv3 output dir>
+        markdown table of per-kernel dispatch counts and durations;
+    python -m decode_kv_cache_amd.profiling traffic --workload W --fetch D1 --write D2 \\
+            --copy-fetch D3 --copy-write D4 --copy-mib M
+        per-launch HBM bytes of every kernel from FETCH_SIZE / WRITE_SIZE runs,
+        each scaled by what the same counter reads for the copy; updates
+        profiles/traffic.json (keyed by workload and the kernel-source hash)
+        and prints a markdown summary.
+
+FETCH_SIZE and WRITE_SIZE are rocprofv3's derived L2-to-memory counters, in
+KiB per dispatch.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def kernel_source_hash() -> str:
+    """Hash of every kernel source; a stored measurement is valid for it only."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "decode_kv_cache_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(name: str) -> str:
+    s = name.replace("void ", "").split("(")[0]
+    for pre in ("kara::(anonymous namespace)::", "kara::"):
+        s = s.replace(pre, "")
+    return s.strip()
+
+
+def _files(d, pattern):
+    return sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True))
+
+
+def counter_means(d: str, counter: str) -> dict:
+    """Mean over dispatches of `counter` per kernel (summing the rows of one dispatch)."""
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    for f in _files(d, "*counter_collection.csv"):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Counter_Name") != counter:
+                    continue
+                per[short_name(r.get("Kernel_Name", ""))][r.get("Dispatch_Id")] += float(r["Counter_Value"])
+    return {k: sum(v.values()) / len(v) for k, v in per.items() if v}
+
+
+def kernel_stats(d: str) -> list:
+    rows = []
+    for f in _files(d, "*kernel_stats.csv"):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                rows.append((short_name(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                             float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    return rows
+
+
+def cmd_copy(a):
+    import torch
+    n = a.mib * 1024 * 1024 // 4
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(a.reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(f"copied {a.mib} MiB x {a.reps} with torch.neg (reads and writes every byte once)", flush=True)
+
+
+def cmd_stats(a):
+    print("| Kernel | Calls | Avg (us) | Min (us) | Max (us) | % of GPU time |")
+    print("|---|---|---|---|---|---|")
+    for name, calls, avg, mn, mx, pct in kernel_stats(a.dir):
+        print(f"| {name} | {calls} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {pct:.2f} |")
+
+
+def cmd_traffic(a):
+    fetch = counter_means(a.fetch, "FETCH_SIZE")
+    write = counter_means(a.write, "WRITE_SIZE")
+    cf = counter_means(a.copy_fetch, "FETCH_SIZE")
+    cw = counter_means(a.copy_write, "WRITE_SIZE")
+    kib = a.copy_mib * 1024.0
+    ck = [k for k in cf if "neg" in k.lower()] or list(cf)
+    f_fac = max(cf[k] for k in ck) / kib
+    w_fac = max(cw[k] for k in ck if k in cw) / kib
+    print(f"copy calibration ({a.copy_mib} MiB read + written): FETCH_SIZE reads {f_fac:.4f} x, "
+          f"WRITE_SIZE {w_fac:.4f} x the bytes moved")
+    print()
+    print("| Kernel | FETCH_SIZE (KiB/dispatch) | WRITE_SIZE (KiB/dispatch) | HBM bytes per launch (scaled) |")
+    print("|---|---|---|---|")
+    rec = {}
+    for k in sorted(set(fetch) | set(write)):
+        if "kara" not in k and not any(t in k for t in ("score", "select", "compact", "finalize", "decode_attn",
+                                                         "row_lse", "col_mass")):
+            continue
+        fb = fetch.get(k, 0.0) * 1024 / f_fac
+        wb = write.get(k, 0.0) * 1024 / w_fac
+        rec[k] = {"fetch_bytes": fb, "write_bytes": wb, "bytes": fb + wb}
+        print(f"| {k} | {fetch.get(k, 0.0):.0f} | {write.get(k, 0.0):.0f} | {fb + wb:.4g} |")
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            data = json.load(f)
+    score = [v["bytes"] for k, v in rec.items() if "score" in k or "row_lse" in k or "col_mass" in k]
+    data[a.workload] = {"kernel_hash": kernel_source_hash(), "copy_factor_fetch": f_fac,
+                        "copy_factor_write": w_fac, "kernels": rec,
+                        "score_bytes_per_launch": sum(score) if score else None}
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1)
+
+
+def main(argv=None):
+    p = argparse.ArgumentParser(prog="python -m decode_kv_cache_amd.profiling")
+    sub = p.add_subparsers(dest="cmd", required=True)
+    c = sub.add_parser("copy")
+    c.add_argument("--mib", type=int, default=2048)
+    c.add_argument("--reps", type=int, default=3)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    t = sub.add_parser("traffic")
+    t.add_argument("--workload", required=True)
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--copy-fetch", required=True)
+    t.add_argument("--copy-write", required=True)
+    t.add_argument("--copy-mib", type=int, required=True)
+    a = p.parse_args(argv)
+    {"copy": cmd_copy, "stats": cmd_stats, "traffic": cmd_traffic}[a.cmd](a)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
