@@ -233,6 +233,32 @@ def main():
                     "frac": round(cbytes / t_c / 1e9 / PEAK_HBM_GBS, 4),
                     "algorithmic": f"4*B*d*elem = {4 * B * d * shape.elem_bytes} B per unit x {shape.units} units"}
 
+    # the same step in one launch (kara_compress_fused), where offered
+    fused = None
+    if K.kara_compress_fused_supported(cfg):
+        done = torch.zeros(S, dtype=torch.int32, device=dev)
+
+        def fused_step():
+            K.kara_compress_fused(cfg, wl.q, wl.k_pool, wl.v_pool, wl.block_tables, wl.prior_lens, scores, kept,
+                                  seq_lens, freed, nfreed, done, stream=st)
+
+        for _ in range(a.warmup):
+            restore()
+            fused_step()
+        torch.cuda.synchronize()
+        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(a.steps)]
+        for i in range(a.steps):
+            restore()
+            fev[i][0].record(st)
+            fused_step()
+            fev[i][1].record(st)
+        torch.cuda.synchronize()
+        ms_fused = float(np.mean([e[0].elapsed_time(e[1]) for e in fev]))
+        fused = {"call": "kara_compress_fused (score + select + compact + table rewrite, one launch)",
+                 "ms_per_step": round(ms_fused, 4), "value": round(tokens / (ms_fused / 1e3), 1),
+                 "vs_three_calls": round(ms_step / ms_fused, 4)}
+        log(f"[bench] one-launch pipeline {ms_fused:.3f} ms/step ({ms_step / ms_fused:.3f}x the three calls)")
+
     consumer = None
     if a.consumer_reps > 0:
         from decode_kv_cache_amd.workloads import decode_queries
@@ -290,6 +316,7 @@ def main():
                       "compact": round(float(np.mean(t_cmp)), 4)},
         "roofline": roof,
         "compact_roofline": compact_roof,
+        "fused_pipeline": fused,
         "decode_attention": consumer,
         "cpu_baseline": cpu,
         "kernel_hash": khash,

@@ -16,6 +16,9 @@ hipError_t launch_compact(const Geo& g, int dtype, void* kc, void* vc, int32_t* 
 hipError_t launch_validate(const Geo& g, const int32_t* tables, const int32_t* prior, int32_t* bad,
                            hipStream_t st);
 size_t decode_attn_workspace_bytes(const Geo& g);
+hipError_t launch_pipeline(const Geo& g, const void* q, void* kc, void* vc, int32_t* tables, const int32_t* prior,
+                           float* scores, int32_t* kept, uint8_t* mask, int32_t* seq_lens, int32_t* freed,
+                           int32_t* num_freed, int max_freed, int32_t* done, hipStream_t st);
 int decode_attn_splits(const Geo& g);
 hipError_t launch_decode_attn(const Geo& g, int dtype, const void* q, const void* kc, const void* vc,
                               const int32_t* tables, const int32_t* lens, float* out, float* ws, hipStream_t st);
@@ -135,6 +138,27 @@ int kara_select_chunks_bridged(const kara_config* cfg, int32_t gap, const float*
   if (cfg->num_seqs == 0) return KARA_OK;
   if (!scores || !kept) return KARA_ENULL;
   return hip_status(kara::launch_select(geo(cfg), gap, scores, kept, mask, (hipStream_t)stream));
+}
+
+int kara_compress_fused_supported(const kara_config* cfg) {
+  if (check(cfg) != KARA_OK) return 0;
+  return kara::fused_score_supported(geo(cfg), cfg->dtype) ? 1 : 0;
+}
+
+int kara_compress_fused(const kara_config* cfg, const void* q, void* k_cache, void* v_cache, int32_t* block_tables,
+                        const int32_t* prior_lens, float* scores, int32_t* kept, uint8_t* mask, int32_t* seq_lens,
+                        int32_t* freed_blocks, int32_t* num_freed, int32_t* done, void* stream) {
+  int s = check(cfg);
+  if (s) return s;
+  const kara::Geo g = geo(cfg);
+  if (!kara::fused_score_supported(g, cfg->dtype)) return KARA_ENOTIMPL;
+  if (cfg->num_seqs == 0) return KARA_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !prior_lens || !scores || !kept || !seq_lens || !freed_blocks ||
+      !num_freed || !done)
+    return KARA_ENULL;
+  return hip_status(kara::launch_pipeline(g, q, k_cache, v_cache, block_tables, prior_lens, scores, kept, mask,
+                                          seq_lens, freed_blocks, num_freed, kara_max_freed(cfg), done,
+                                          (hipStream_t)stream));
 }
 
 size_t kara_decode_attention_workspace_bytes(const kara_config* cfg) {

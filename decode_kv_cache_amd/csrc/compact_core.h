@@ -1,0 +1,88 @@
+// In-place compaction of one unit's kept window rows and the per-sequence
+// block-table rewrite, as device functions shared by the compaction kernels
+// and the single-launch pipeline.
+//
+// Kara's English abstract: the method is adapted to PagedAttention and lowers
+// KV-cache memory.  Recorded reading: for unit (n, l, g) and r < B, logical
+// slot L+r takes the old row of slot L+kept[r] (K and V); afterwards, per
+// sequence, the table entries of logical blocks ceil((L+B)/bs) ..
+// ceil((L+W)/bs)-1 are handed back in order and set to -1.
+//
+// In-place safety: kept is strictly ascending, so kept[r] >= r.  The rows of
+// a unit are walked in ascending chunks: a chunk is read into registers, the
+// reads are waited for, the workgroup synchronises, then the chunk is
+// written.  A chunk's writes land on slots < L + (end of chunk) while every
+// later source is at or past that point, and every source a later write could
+// hit was read before the barrier of its own chunk.
+#pragma once
+
+#include "kara_device.h"
+
+namespace kara {
+
+// rows are streamed once: non-temporal loads and stores keep them out of the caches
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Copy the B kept rows of one (unit, pool) into place.  kl = the unit's kept
+// list (global or LDS); NT threads, VEC 16-byte vectors per thread per chunk.
+template <int NT, int ROWBYTES, int VEC>
+__device__ __forceinline__ void compact_unit_rows(const Geo& g, unsigned char* __restrict__ pool,
+                                                  const int32_t* __restrict__ trow, int layer, int kvh, int L,
+                                                  const int32_t* kl, int esize) {
+  constexpr int TPR = ROWBYTES / 16;                  // threads per row
+  constexpr int RPP = NT / TPR;                       // rows per pass
+  constexpr int CH = RPP * VEC;                       // rows per chunk
+  const int t = threadIdx.x;
+  const int part = t % TPR;
+  const int rsub = t / TPR;
+  for (int c0 = 0; c0 < g.B; c0 += CH) {
+    u32x4 buf[VEC];
+    long long dst[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+      const int r = c0 + v * RPP + rsub;
+      dst[v] = -1;
+      if (r < g.B) {
+        const int j = kl[r];
+        const long long so = (j >= 0 && j < g.W) ? slot_offset(g, trow, layer, kvh, L + j) : -1;
+        const long long d = slot_offset(g, trow, layer, kvh, L + r);
+        if (so >= 0 && d >= 0) {
+          buf[v] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pool + so * esize + part * 16));
+          dst[v] = d;
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // every read of this chunk has returned
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < VEC; ++v)
+      if (dst[v] >= 0) __builtin_nontemporal_store(buf[v], reinterpret_cast<u32x4*>(pool + dst[v] * esize + part * 16));
+  }
+}
+
+// Freed list, table truncation and new length of sequence n (one thread).
+__device__ inline void finalize_sequence(const Geo& g, int n, int32_t* __restrict__ tables,
+                                         const int32_t* __restrict__ prior, int32_t* __restrict__ seq_lens,
+                                         int32_t* __restrict__ freed, int32_t* __restrict__ num_freed,
+                                         int max_freed) {
+  const int L = prior[n];
+  int32_t* row = tables + (long long)n * g.max_blocks;
+  int32_t* fr = freed + (long long)n * max_freed;
+  int cnt = 0;
+  if (L >= 0) {
+    const long long nb_old_ll = ((long long)L + g.W + g.bs - 1) >> g.bs_shift;
+    const int nb_old = (int)min(nb_old_ll, (long long)g.max_blocks);
+    const int nb_new = (int)min((((long long)L + g.B + g.bs - 1) >> g.bs_shift), (long long)nb_old);
+    for (int b = nb_new; b < nb_old && cnt < max_freed; ++b) {
+      fr[cnt++] = row[b];
+      row[b] = -1;
+    }
+    seq_lens[n] = L + g.B;
+  } else {
+    seq_lens[n] = L;
+  }
+  num_freed[n] = cnt;
+  for (int k = cnt; k < max_freed; ++k) fr[k] = -1;
+}
+
+}  // namespace kara

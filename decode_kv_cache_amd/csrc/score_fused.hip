@@ -19,7 +19,9 @@
 //     blocks of the unit; they are reduced over the 16 query lanes once, at
 //     the end.
 // Each logit is computed once and exponentiated once.
+#include "compact_core.h"
 #include "kara_device.h"
+#include "select_core.h"
 
 namespace kara {
 
@@ -67,7 +69,8 @@ __device__ __forceinline__ float group_sum(float v) {
 template <bool MASK>
 __device__ __forceinline__ void fused_unit(const Geo& g, int unit, const __bf16* __restrict__ q,
                                            const bf16x8 (&kf)[KTW][4], int key0, unsigned char (*qtile)[QB * QLROW],
-                                           float2 (*red)[QB][FW], float* __restrict__ scores) {
+                                           float2 (*red)[QB][FW], float* __restrict__ scores,
+                                           uint32_t* keys_lds) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int qlane = lane & 15, grp = lane >> 4;
@@ -193,7 +196,10 @@ __device__ __forceinline__ void fused_unit(const Geo& g, int unit, const __bf16*
       for (int rr = 0; rr < 2; ++rr) {
         const int r = 2 * (qlane & 1) + rr;
         const int key = kbase + 16 * t + r;
-        if (key < g.W) out[key] = colacc[t][r];
+        if (key < g.W) {
+          out[key] = colacc[t][r];
+          if (keys_lds) keys_lds[key] = order_key(colacc[t][r]);
+        }
       }
     }
 }
@@ -232,9 +238,9 @@ __global__ __launch_bounds__(FTHREADS, 1) void fused_score_kernel(Geo g, const _
   }
   // every wave of the workgroup takes the same branch (it depends on W only)
   if (g.W >= FW * KTW * 16)
-    fused_unit<false>(g, unit, q, kf, key0, qtile, red, scores);
+    fused_unit<false>(g, unit, q, kf, key0, qtile, red, scores, nullptr);
   else
-    fused_unit<true>(g, unit, q, kf, key0, qtile, red, scores);
+    fused_unit<true>(g, unit, q, kf, key0, qtile, red, scores, nullptr);
 }
 
 hipError_t launch_fused_score(const Geo& g, const void* q, const void* kc, const int32_t* tables,
@@ -243,6 +249,91 @@ hipError_t launch_fused_score(const Geo& g, const void* q, const void* kc, const
   if (units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(fused_score_kernel, dim3((unsigned)units), dim3(FTHREADS), 0, st, g, (const __bf16*)q,
                      (const __bf16*)kc, tables, prior, scores);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Single-launch pipeline: the workgroup that scores a unit also selects its
+// kept positions (select_core.h, keys straight from the scores it just
+// produced) and compacts the unit's K and V rows in place (compact_core.h).
+// The block-table rewrite of a sequence must follow every read of that
+// sequence's table, so each workgroup counts itself in done[n] once its
+// compaction has read the table; the workgroup that brings the count to
+// layers * kv_heads rewrites the table and resets the counter to zero.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(FTHREADS, 1) void pipeline_kernel(Geo g, const __bf16* __restrict__ q,
+                                                                unsigned char* __restrict__ kc,
+                                                                unsigned char* __restrict__ vc,
+                                                                int32_t* __restrict__ tables,
+                                                                const int32_t* __restrict__ prior,
+                                                                float* __restrict__ scores, int32_t* __restrict__ kept,
+                                                                uint8_t* __restrict__ mask,
+                                                                int32_t* __restrict__ seq_lens,
+                                                                int32_t* __restrict__ freed,
+                                                                int32_t* __restrict__ num_freed, int max_freed,
+                                                                int32_t* __restrict__ done) {
+  __shared__ __align__(16) unsigned char qtile[2][QB * QLROW];
+  __shared__ __align__(16) float2 red[2][QB][FW];
+  __shared__ __align__(16) uint32_t keys[FW * KTW * 16];
+  __shared__ __align__(16) int32_t kl[FW * KTW * 16];
+  __shared__ uint8_t flags[FW * KTW * 16];
+  __shared__ SelScratch<FTHREADS> sh;
+  __shared__ int last;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int qlane = lane & 15, grp = lane >> 4;
+  const int unit = blockIdx.x;
+  const int kvh = unit % g.Hkv;
+  const int layer = (unit / g.Hkv) % g.Lyr;
+  const int n = unit / (g.Hkv * g.Lyr);
+  const int L = prior[n];
+  const int32_t* trow = tables + (long long)n * g.max_blocks;
+
+  {
+    const int key0 = wave * KTW * 16;
+    const PagedRows pr = paged_rows(g, trow, layer, kvh, L, 2);
+    bf16x8 kf[KTW][4];
+#pragma unroll
+    for (int t = 0; t < KTW; ++t) {
+      const int j = min(key0 + 16 * t + qlane, g.W - 1);
+      const uint4* src = reinterpret_cast<const uint4*>(kc + paged_row(pr, L + j) + grp * 64);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint4 v = src[s];
+        __builtin_memcpy(&kf[t][s], &v, 16);
+      }
+    }
+    if (g.W >= FW * KTW * 16)
+      fused_unit<false>(g, unit, q, kf, key0, qtile, red, scores, keys);
+    else
+      fused_unit<true>(g, unit, q, kf, key0, qtile, red, scores, keys);
+  }
+  select_unit<FTHREADS, FW * KTW * 16 / FTHREADS>(g, 0, keys, flags, sh, kl, kept + (long long)unit * g.B,
+                        mask ? mask + (long long)unit * g.W : nullptr);
+  __syncthreads();                                   // kl complete
+  compact_unit_rows<FTHREADS, FD * 2, 8>(g, kc, trow, layer, kvh, L, kl, 2);
+  compact_unit_rows<FTHREADS, FD * 2, 8>(g, vc, trow, layer, kvh, L, kl, 2);
+  __syncthreads();                                   // every table read of this workgroup is done
+  if (tid == 0) {
+    __threadfence();
+    last = atomicAdd(&done[n], 1) == g.Lyr * g.Hkv - 1;
+  }
+  __syncthreads();
+  if (last && tid == 0) {
+    __threadfence();
+    finalize_sequence(g, n, tables, prior, seq_lens, freed, num_freed, max_freed);
+    done[n] = 0;
+  }
+}
+
+hipError_t launch_pipeline(const Geo& g, const void* q, void* kc, void* vc, int32_t* tables, const int32_t* prior,
+                           float* scores, int32_t* kept, uint8_t* mask, int32_t* seq_lens, int32_t* freed,
+                           int32_t* num_freed, int max_freed, int32_t* done, hipStream_t st) {
+  const long long units = (long long)g.S * g.Lyr * g.Hkv;
+  if (units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(pipeline_kernel, dim3((unsigned)units), dim3(FTHREADS), 0, st, g, (const __bf16*)q,
+                     (unsigned char*)kc, (unsigned char*)vc, tables, prior, scores, kept, mask, seq_lens, freed,
+                     num_freed, max_freed, done);
   return hipGetLastError();
 }
 

@@ -163,6 +163,26 @@ int kara_compact_paged(const kara_config* cfg, void* k_cache, void* v_cache, int
                        int32_t* freed_blocks, int32_t* num_freed, void* stream);
 
 /*
+ * The whole step in one launch: scores, Token2Chunk selection and in-place
+ * compaction of every unit, and every sequence's block-table rewrite, with
+ * exactly the results of kara_score_window + kara_select_chunks +
+ * kara_compact_paged (same layouts and outputs; mask may be NULL).  One
+ * workgroup scores a unit, selects from the scores it produced and compacts
+ * the unit's rows; the last workgroup of a sequence to finish rewrites that
+ * sequence's table.  `done` is int32 [num_seqs] device memory that must hold
+ * zeros before the first call; every call returns it to zeros.  Calls that
+ * share a `done` array must not run concurrently.  Available when
+ * kara_compress_fused_supported(cfg) is 1 (bf16, head_dim 128, W <= 1024),
+ * else KARA_ENOTIMPL.  Other errors: KARA_EINVAL, KARA_ENULL, KARA_EHIP.
+ */
+int kara_compress_fused_supported(const kara_config* cfg);
+
+int kara_compress_fused(const kara_config* cfg, const void* q, void* k_cache, void* v_cache,
+                        int32_t* block_tables, const int32_t* prior_lens, float* scores, int32_t* kept,
+                        uint8_t* mask, int32_t* seq_lens, int32_t* freed_blocks, int32_t* num_freed,
+                        int32_t* done, void* stream);
+
+/*
  * Consumer of the compacted cache: one decode step of paged attention (Kara
  * abstract: the compressed window lives in a PagedAttention store whose
  * smaller footprint raises output throughput).  For every sequence n, layer
