@@ -44,6 +44,7 @@ def parse():
     p.add_argument("--workload", default="llama8b_b64")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-peaks", action="store_true", help="skip the achievable-peak probes")
     p.add_argument("--consumer-reps", type=int, default=10,
                    help="timed decode-attention passes over the cache before and after compaction (0: skip)")
     return p.parse_args()
@@ -298,6 +299,19 @@ def main():
                     "splits": K.kara_decode_attention_splits(cfg)}
         log(f"[bench] decode attention: compacted {tc:.3f} ms ({bc / tc / 1e6:.0f} GB/s), full {tf:.3f} ms")
 
+    achievable = None
+    if not a.no_peaks:
+        from decode_kv_cache_amd.profiling import achievable_peaks
+        achievable = achievable_peaks()
+        log(f"[bench] achievable peaks: {achievable}")
+        roof["frac_of_achievable"] = round(roof["achieved"] / achievable["mfma_bf16_tflops"], 4) \
+            if shape.dtype == "bf16" else None
+        compact_roof["frac_of_achievable"] = round(compact_roof["achieved"] /
+                                                   achievable["hbm_copy_GBps_read_plus_write"], 4)
+        if consumer:
+            consumer["roofline"]["frac_of_achievable"] = round(consumer["roofline"]["achieved"] /
+                                                               achievable["hbm_read_GBps"], 4)
+
     cpu = None
     if not a.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on a CPU sample")
@@ -314,11 +328,13 @@ def main():
                    "key_model": shape.key_model, "plants": shape.plants, "parallelism": "single GPU"},
         "stages_ms": {"score": round(float(np.mean(t_score)), 4), "select": round(float(np.mean(t_sel)), 4),
                       "compact": round(float(np.mean(t_cmp)), 4)},
+        "step_ms_median": round(float(np.median(ms)), 4), "step_ms_min": round(float(np.min(ms)), 4),
         "roofline": roof,
         "compact_roofline": compact_roof,
         "fused_pipeline": fused,
         "decode_attention": consumer,
         "cpu_baseline": cpu,
+        "achievable_peaks": achievable,
         "kernel_hash": khash,
         "wall_ms_per_step_incl_restore": round(wall / a.steps * 1e3, 3),
     }

@@ -1,4 +1,5 @@
-"""Build libkara.so in-tree with hipcc for gfx950.
+"""Build libkara.so (the Kara library) and libkara_probes.so (achievable-peak
+probes used by the measurements) in-tree with hipcc for gfx950.
 
     python -m decode_kv_cache_amd.build
 """
@@ -15,6 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkara.so")
 SOURCES = ["api.hip", "score.hip", "score_fused.hip", "select.hip", "compact.hip", "decode_attn.hip"]
+PROBES_LIB = os.path.join(PKG, "libkara_probes.so")
+PROBES_SOURCES = ["probes.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -36,11 +39,18 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = True, out: str = LIB, csrc: str = CSRC, extra=()) -> str:
-    """Compile every HIP source into libkara.so next to this file; return its path."""
+def build(verbose: bool = True, out: str = LIB, csrc: str = CSRC, extra=(), sources=None) -> str:
+    """Compile the library's HIP sources into libkara.so next to this file
+    (and the probes into libkara_probes.so); return the library's path."""
+    if out == LIB and sources is None:
+        _compile(verbose, PROBES_LIB, csrc, extra, PROBES_SOURCES)
+    return _compile(verbose, out, csrc, extra, sources or SOURCES)
+
+
+def _compile(verbose, out, csrc, extra, sources) -> str:
     tmp = out + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, *extra, f"-I{INCLUDE}", f"-I{csrc}",
-           *[os.path.join(csrc, s) for s in SOURCES], "-o", tmp]
+           *[os.path.join(csrc, s) for s in sources], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

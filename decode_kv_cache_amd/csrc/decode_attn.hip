@@ -24,8 +24,7 @@
 
 namespace kara {
 
-namespace {
-
+// (kernels live in namespace kara so that profilers print their names)
 constexpr int DA_WAVES = 4;
 constexpr int DA_THREADS = 64 * DA_WAVES;
 constexpr int DA_TBL = 4096;   // block-table entries one workgroup stages in LDS
@@ -352,7 +351,7 @@ struct AttnPlan {
   size_t ws_bytes;
 };
 
-AttnPlan plan_of(const Geo& g) {
+static AttnPlan plan_of(const Geo& g) {
   AttnPlan p;
   p.GM = g.G <= 1 ? 1 : g.G <= 2 ? 2 : g.G <= 4 ? 4 : 8;
   p.hchunks = (g.G + p.GM - 1) / p.GM;
@@ -390,8 +389,6 @@ hipError_t launch_t(const AttnGeo& a, int GM, long long wgs, const void* q, cons
   }
   return hipGetLastError();
 }
-
-}  // namespace
 
 size_t decode_attn_workspace_bytes(const Geo& g) { return plan_of(g).ws_bytes; }
 

@@ -1,0 +1,120 @@
+// Achievable-peak probes for gfx950, built into libkara_probes.so (not part
+// of the Kara library).  Each launcher enqueues one kernel on `stream`; the
+// caller times it with events and divides the work stated beside it.
+//
+//   kara_probe_mfma  : blocks x 4 waves, each iters x 4 MFMA 32x32x16 bf16
+//                      (32768 FLOP per wave per MFMA), accumulators independent
+//   kara_probe_exp   : blocks x 256 lanes, each iters x 8 v_exp_f32
+//   kara_probe_fma   : blocks x 256 lanes, each iters x 8 v_fma_f32
+//   kara_probe_read  : reads `bytes` once (16-byte non-temporal loads, 8 in
+//                      flight per thread) and writes one float per thread
+//   kara_probe_copy  : copies `bytes` (reads and writes each byte once)
+// Work sizes must keep every index inside the buffers: bytes a multiple of
+// 16, out holding blocks * 256 floats (read: grid * 256 floats, grid given).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kara_probes.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void probe_mfma(float* out, int iters) {
+  bf16x8 a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(threadIdx.x * 1e-3f);
+    b[i] = (__bf16)(i * 1e-3f);
+  }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int i = 0; i < iters; ++i) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+  }
+  float s = 0.f;
+  for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+template <bool EXP>
+__global__ __launch_bounds__(256) void probe_valu(float* out, int iters, float a) {
+  float x[8];
+  for (int e = 0; e < 8; ++e) x[e] = threadIdx.x * 1e-3f + 0.1f * e;
+  for (int i = 0; i < iters; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = EXP ? __builtin_amdgcn_exp2f(x[e] * a) : __builtin_fmaf(x[e], a, 0.5f);
+  float s = 0.f;
+  for (int e = 0; e < 8; ++e) s += x[e];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) void probe_read(const u32x4* __restrict__ src, size_t n, float* out) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  unsigned acc = 0;
+  for (; i + 7 * stride < n; i += 8 * stride) {
+    u32x4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = __builtin_nontemporal_load(src + i + k * stride);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+  }
+  for (; i < n; i += stride) acc ^= __builtin_nontemporal_load(src + i).x;
+  out[blockIdx.x * blockDim.x + threadIdx.x] = (float)(acc & 1u);
+}
+
+__global__ __launch_bounds__(256) void probe_copy(const u32x4* __restrict__ src, u32x4* __restrict__ dst, size_t n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  for (; i + stride < n; i += 2 * stride) {
+    const u32x4 a = __builtin_nontemporal_load(src + i);
+    const u32x4 b = __builtin_nontemporal_load(src + i + stride);
+    __builtin_nontemporal_store(a, dst + i);
+    __builtin_nontemporal_store(b, dst + i + stride);
+  }
+  for (; i < n; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+int status(hipError_t e) { return e == hipSuccess ? 0 : (int)e; }
+
+}  // namespace
+
+extern "C" {
+
+int kara_probe_mfma(float* out, int blocks, int iters, void* stream) {
+  if (!out || blocks < 1 || iters < 1) return -1;
+  hipLaunchKernelGGL(probe_mfma, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters);
+  return status(hipGetLastError());
+}
+
+int kara_probe_exp(float* out, int blocks, int iters, void* stream) {
+  if (!out || blocks < 1 || iters < 1) return -1;
+  hipLaunchKernelGGL(probe_valu<true>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters, 0.999f);
+  return status(hipGetLastError());
+}
+
+int kara_probe_fma(float* out, int blocks, int iters, void* stream) {
+  if (!out || blocks < 1 || iters < 1) return -1;
+  hipLaunchKernelGGL(probe_valu<false>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters, 0.999f);
+  return status(hipGetLastError());
+}
+
+int kara_probe_read(const void* src, size_t bytes, float* out, int grid, void* stream) {
+  if (!src || !out || grid < 1 || (bytes & 15)) return -1;
+  hipLaunchKernelGGL(probe_read, dim3(grid), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src, bytes / 16,
+                     out);
+  return status(hipGetLastError());
+}
+
+int kara_probe_copy(const void* src, void* dst, size_t bytes, int grid, void* stream) {
+  if (!src || !dst || grid < 1 || (bytes & 15)) return -1;
+  hipLaunchKernelGGL(probe_copy, dim3(grid), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src, (u32x4*)dst,
+                     bytes / 16);
+  return status(hipGetLastError());
+}
+
+}  // extern "C"

@@ -4,6 +4,9 @@
         a plain device copy of a known size (an elementwise torch kernel that
         reads and writes every byte once), run under ``rocprofv3 --pmc`` to
         calibrate FETCH_SIZE / WRITE_SIZE against bytes actually moved;
+    python -m decode_kv_cache_amd.profiling peaks
+        achievable peaks on this GPU from libkara_probes.so (MFMA bf16 loop,
+        v_exp_f32 and fp32 FMA rates, HBM read and copy bandwidth), as JSON;
     python -m decode_kv_cache_amd.profiling stats <rocprofv3 output dir>
         markdown table of per-kernel dispatch counts and durations;
     python -m decode_kv_cache_amd.profiling traffic --workload W --fetch D1 --write D2 \\
@@ -73,6 +76,68 @@ def kernel_stats(d: str) -> list:
     return rows
 
 
+def achievable_peaks(device=0) -> dict:
+    """Time the probes of libkara_probes.so with HIP events on one stream."""
+    import ctypes
+
+    import torch
+    path = os.path.join(ROOT, "decode_kv_cache_amd", "libkara_probes.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m decode_kv_cache_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    for name, args in (("kara_probe_mfma", [vp, i32, i32, vp]), ("kara_probe_exp", [vp, i32, i32, vp]),
+                       ("kara_probe_fma", [vp, i32, i32, vp]), ("kara_probe_read", [vp, sz, vp, i32, vp]),
+                       ("kara_probe_copy", [vp, vp, sz, i32, vp])):
+        getattr(lib, name).argtypes = args
+        getattr(lib, name).restype = i32
+    dev = torch.device("cuda", device)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    st = torch.cuda.Stream(device=dev)
+    sptr = ctypes.c_void_p(st.cuda_stream)
+
+    def timed(launch, reps=3):
+        launch()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(st)
+        for _ in range(reps):
+            if launch() != 0:
+                raise RuntimeError("probe launch failed")
+        ev[1].record(st)
+        torch.cuda.synchronize(dev)
+        return ev[0].elapsed_time(ev[1]) / reps / 1e3
+
+    blocks, iters = cus * 8, 4096
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    o = ctypes.c_void_p(out.data_ptr())
+    t = timed(lambda: lib.kara_probe_mfma(o, blocks, iters, sptr))
+    mfma = blocks * 4 * iters * 4 * 32768.0 / t / 1e12
+    t = timed(lambda: lib.kara_probe_exp(o, blocks, iters, sptr))
+    exps = blocks * 256 * iters * 8.0 / t
+    t = timed(lambda: lib.kara_probe_fma(o, blocks, iters, sptr))
+    fmas = blocks * 256 * iters * 8.0 / t
+    nbytes = 4 << 30
+    grid = cus * 64
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+    sp, dp, kp = (ctypes.c_void_p(x.data_ptr()) for x in (src, dst, sink))
+    t = timed(lambda: lib.kara_probe_read(sp, nbytes, kp, grid, sptr))
+    read = nbytes / t / 1e9
+    t = timed(lambda: lib.kara_probe_copy(sp, dp, nbytes, grid, sptr))
+    copy = 2 * nbytes / t / 1e9
+    del src, dst
+    return {"mfma_bf16_tflops": round(mfma, 1), "v_exp_f32_per_s": float(f"{exps:.4g}"),
+            "fma_f32_per_s": float(f"{fmas:.4g}"), "hbm_read_GBps": round(read, 1),
+            "hbm_copy_GBps_read_plus_write": round(copy, 1),
+            "how": "libkara_probes.so: MFMA 32x32x16 bf16 loop, v_exp_f32 / v_fma_f32 chains (8 per lane per "
+                   "iteration), 4 GiB non-temporal read and copy; HIP events over 3 launches after one warm-up"}
+
+
+def cmd_peaks(a):
+    print(json.dumps(achievable_peaks()), flush=True)
+
+
 def cmd_copy(a):
     import torch
     n = a.mib * 1024 * 1024 // 4
@@ -133,6 +198,7 @@ def main(argv=None):
     c = sub.add_parser("copy")
     c.add_argument("--mib", type=int, default=2048)
     c.add_argument("--reps", type=int, default=3)
+    sub.add_parser("peaks")
     s = sub.add_parser("stats")
     s.add_argument("dir")
     t = sub.add_parser("traffic")
@@ -143,7 +209,7 @@ def main(argv=None):
     t.add_argument("--copy-write", required=True)
     t.add_argument("--copy-mib", type=int, required=True)
     a = p.parse_args(argv)
-    {"copy": cmd_copy, "stats": cmd_stats, "traffic": cmd_traffic}[a.cmd](a)
+    {"copy": cmd_copy, "peaks": cmd_peaks, "stats": cmd_stats, "traffic": cmd_traffic}[a.cmd](a)
 
 
 if __name__ == "__main__":

@@ -1,0 +1,38 @@
+/*
+ * kara_probes.h - achievable-peak probes for MI355X (gfx950), exported by
+ * libkara_probes.so.  Measurement tooling beside the Kara library: each call
+ * enqueues one kernel on `stream` (a hipStream_t, NULL = default stream) and
+ * returns 0, -1 for a bad argument, or the HIP error code of the launch.
+ * All pointers are device pointers owned by the caller.
+ */
+#ifndef KARA_PROBES_H_
+#define KARA_PROBES_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* blocks x 4 waves; each wave issues iters x 4 MFMA 32x32x16 bf16 (32768 FLOP each).
+ * out: blocks * 256 floats. */
+int kara_probe_mfma(float* out, int blocks, int iters, void* stream);
+
+/* blocks x 256 lanes; each lane issues iters x 8 exp2 (v_exp_f32).  out: blocks * 256 floats. */
+int kara_probe_exp(float* out, int blocks, int iters, void* stream);
+
+/* blocks x 256 lanes; each lane issues iters x 8 fp32 FMA.  out: blocks * 256 floats. */
+int kara_probe_fma(float* out, int blocks, int iters, void* stream);
+
+/* Reads `bytes` (a multiple of 16) of src once.  out: grid * 256 floats. */
+int kara_probe_read(const void* src, size_t bytes, float* out, int grid, void* stream);
+
+/* Copies `bytes` (a multiple of 16) from src to dst (each byte read and written once). */
+int kara_probe_copy(const void* src, void* dst, size_t bytes, int grid, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KARA_PROBES_H_ */

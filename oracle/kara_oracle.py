@@ -38,7 +38,7 @@ Readings taken where the pages are silent (each is stated where used):
 * R20     bridging variant (not the main rule): neighbouring seeds that leave
   at most ``gap`` positions between them are joined by keeping everything in
   between (the explainers' "keep what lies between two important points").
-* R21/R22 the consumer (decode attention) reads every cached slot [0, seq_len)
+* R25/R26 the consumer (decode attention) reads every cached slot [0, seq_len)
   of the sequence through its block table, scale 1/sqrt(d), GQA as in R4; an
   empty cache yields a zero output.
 * R14-R18 compaction is in place: logical slot L + r receives the row that
@@ -287,7 +287,7 @@ def paged_decode_attention(q_dec, k_pool, v_pool, block_tables, seq_lens, block_
     PagedAttention store and claims lower KV memory and higher output
     throughput; the decode step that reads the cache is ordinary scaled
     dot-product attention over the logical slots [0, seq_len) reached through
-    the block table (reading R21: the query attends every cached slot, no
+    the block table (reading R25: the query attends every cached slot, no
     mask inside the cache; query head h reads KV head h // G as in R4).
 
     q_dec        [S][layers][Hq][d]
@@ -295,7 +295,7 @@ def paged_decode_attention(q_dec, k_pool, v_pool, block_tables, seq_lens, block_
     block_tables [S][max_blocks];  seq_lens [S]
     Returns o [S][layers][Hq][d] in fp64:
         o = sum_j softmax_j(q . k_j / sqrt(d)) v_j ;  seq_len 0 gives o = 0
-    (reading R22: an empty cache contributes nothing).
+    (reading R26: an empty cache contributes nothing).
     """
     S, layers, Hq, d = q_dec.shape
     Hkv = k_pool.shape[2]

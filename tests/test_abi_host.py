@@ -14,8 +14,8 @@ from tests.conftest import ROOT
 HEADER = os.path.join(ROOT, "include", "kara.h")
 
 
-def _declared():
-    text = open(HEADER).read()
+def _declared(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(kara_[a-z_]+)\s*\(", text)))
 
@@ -27,6 +27,14 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(K.EXPORTED_SYMBOLS)
+
+
+def test_probe_library_exports_its_declared_symbols():
+    lib = ctypes.CDLL(os.path.join(ROOT, "decode_kv_cache_amd", "libkara_probes.so"))
+    names = _declared(os.path.join(ROOT, "include", "kara_probes.h"))
+    assert len(names) == 5
+    for name in names:
+        assert hasattr(lib, name), name
 
 
 def _cfg(name="llama8b_b64", **kw):

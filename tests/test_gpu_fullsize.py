@@ -96,3 +96,92 @@ def test_full_size_sampled(name):
         assert np.array_equal(_bits(_unit_rows(wl, wl.v_pool, n, layer, g, L - head, head)), d["vhead"])
     del wl, out
     torch.cuda.empty_cache()
+
+
+def _sample_units(s, rng, k=6):
+    S, Lyr, Hkv = s.num_seqs, s.num_layers, s.num_kv_heads
+    units = {(0, 0, 0), (S - 1, Lyr - 1, Hkv - 1)}
+    while len(units) < k:
+        units.add((int(rng.integers(S)), int(rng.integers(Lyr)), int(rng.integers(Hkv))))
+    return sorted(units)
+
+
+@pytest.mark.parametrize("name", ["llama8b_b1", "llama8b_b64"])
+def test_full_size_pipeline(name):
+    """kara_compress_fused at full size: scores and kept lists equal to the
+    separate calls on the same input, every table and length exact, and
+    sampled units' compacted rows exact against the oracle."""
+    from decode_kv_cache_amd import kara as K
+    from tests.kara_harness import Outputs, config_of
+    s = shape_by_name(name)
+    print(f"[{name}] generating", flush=True)
+    wl = make_workload(s, "cuda")
+    S, Lyr, Hkv, W, B = s.num_seqs, s.num_layers, s.num_kv_heads, s.window, s.budget
+    cfg = config_of(wl)
+    ref = Outputs(cfg, "cuda")
+    K.kara_score_window(cfg, wl.q, wl.k_pool, wl.block_tables, wl.prior_lens, ref["scores"], ref.ws)
+    K.kara_select_chunks(cfg, ref["scores"], ref["kept"])
+    rng = np.random.default_rng(s.shape_id + 17)
+    units = _sample_units(s, rng)
+    saved = {u: (_bits(_unit_rows(wl, wl.k_pool, *u, int(wl.host_prior_lens[u[0]]), W)),
+                 _bits(_unit_rows(wl, wl.v_pool, *u, int(wl.host_prior_lens[u[0]]), W))) for u in units}
+    out = Outputs(cfg, "cuda")
+    done = torch.zeros(S, dtype=torch.int32, device="cuda")
+    print(f"[{name}] one-launch pipeline", flush=True)
+    K.kara_compress_fused(cfg, wl.q, wl.k_pool, wl.v_pool, wl.block_tables, wl.prior_lens, out["scores"],
+                          out["kept"], out["seq_lens"], out["freed"], out["num_freed"], done)
+    torch.cuda.synchronize()
+    assert torch.all(done == 0)
+    assert torch.equal(out["scores"], ref["scores"]) and torch.equal(out["kept"], ref["kept"])
+    tables, lens = wl.block_tables.cpu().numpy(), out["seq_lens"].cpu().numpy()
+    freed, nfreed = out["freed"].cpu().numpy(), out["num_freed"].cpu().numpy()
+    for n in range(S):
+        row, fr, new_len = oracle.rewrite_block_table(wl.host_tables[n], int(wl.host_prior_lens[n]), W, B,
+                                                      s.block_size)
+        assert np.array_equal(tables[n], row) and lens[n] == new_len and nfreed[n] == fr.size
+        assert freed[n, :fr.size].tolist() == fr.tolist()
+    kept_h = out["kept"].cpu().numpy()
+    for u in units:
+        L = int(wl.host_prior_lens[u[0]])
+        kk = kept_h[u]
+        assert np.array_equal(_bits(_unit_rows(wl, wl.k_pool, *u, L, W)), oracle.compact_window_rows(saved[u][0], kk))
+        assert np.array_equal(_bits(_unit_rows(wl, wl.v_pool, *u, L, W)), oracle.compact_window_rows(saved[u][1], kk))
+    del wl, out, ref
+    torch.cuda.empty_cache()
+
+
+def test_full_size_decode_attention_after_compaction():
+    """Decode attention over the compacted 64-sequence 8B cache (random prior
+    context) against the oracle for every query head of sampled units."""
+    from decode_kv_cache_amd import kara as K
+    from decode_kv_cache_amd.workloads import decode_queries, fill_prior_context
+    from tests.test_gpu_attention import ATTN_ATOL, ATTN_RTOL
+    s = shape_by_name("llama8b_b64")
+    print("[attention] generating", flush=True)
+    wl = make_workload(s, "cuda")
+    fill_prior_context(wl)
+    q_dec = decode_queries(s, "cuda")
+    print("[attention] compressing", flush=True)
+    cfg, out = run_step(wl, with_mask=False)
+    att = torch.full((s.num_seqs, s.num_layers, s.num_q_heads, s.head_dim), float("nan"), device="cuda")
+    wsb = K.kara_decode_attention_workspace_bytes(cfg)
+    ws = torch.empty(wsb // 4 + 64, dtype=torch.float32, device="cuda") if wsb else None
+    K.kara_decode_attention(cfg, q_dec, wl.k_pool, wl.v_pool, wl.block_tables, out["seq_lens"], att, ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(att).all()
+    att_h = att.cpu().numpy().astype(np.float64)
+    G, d = s.group, s.head_dim
+    rng = np.random.default_rng(99)
+    for (n, layer, g) in _sample_units(s, rng):
+        T = int(wl.host_prior_lens[n]) + s.budget
+        print(f"[attention] oracle on unit {(n, layer, g)}, {T} slots", flush=True)
+        Kd = _unit_rows(wl, wl.k_pool, n, layer, g, 0, T).float().double().cpu().numpy()
+        Vd = _unit_rows(wl, wl.v_pool, n, layer, g, 0, T).float().double().cpu().numpy()
+        for h in range(g * G, (g + 1) * G):
+            q = q_dec[n, layer, h].float().double().cpu().numpy()
+            z = Kd @ q / np.sqrt(d)
+            p = np.exp(z - z.max())
+            o = (p / p.sum()) @ Vd
+            assert np.all(np.abs(att_h[n, layer, h] - o) <= ATTN_ATOL + ATTN_RTOL * np.abs(o)), (n, layer, h)
+    del wl, out
+    torch.cuda.empty_cache()
