@@ -86,7 +86,16 @@ __device__ __forceinline__ void fused_unit(const Geo& g, int unit, const __bf16*
   // staging: the 512 threads move 16 rows x 256 bytes, 8 bytes each; tiles are
   // fetched two blocks ahead (two register stages) to cover memory latency
   const int srow = tid >> 5, sbyte = (tid & 31) * 8;
+  // When G divides the block height, a thread's row of block b sits at a
+  // fixed offset plus b times the bytes of QB / G window positions, so the
+  // address is one scalar step per block; otherwise (and for a partial last
+  // block) the row is split into (position, head) by division.
+  const bool lin = (QB % g.G) == 0;
+  const int nfull = g.GW / QB;
+  const long long lstep = lin ? (long long)(QB / g.G) * g.Hq * QROWB : 0;
+  const unsigned char* qlin = qbytes + ((long long)(srow / g.G) * g.Hq + srow % g.G) * QROWB + sbyte;
   auto q_fetch = [&](int b) -> uint2 {
+    if (lin && b < nfull) return *reinterpret_cast<const uint2*>(qlin + b * lstep);
     const int row = min(b * QB + srow, g.GW - 1);
     const int qi = row / g.G, qh = row - qi * g.G;
     return *reinterpret_cast<const uint2*>(qbytes + ((long long)qi * g.Hq + qh) * QROWB + sbyte);
@@ -133,11 +142,15 @@ __device__ __forceinline__ void fused_unit(const Geo& g, int unit, const __bf16*
           if (kbase + 16 * t + r >= g.W) acc[t][r] = -INFINITY;
     }
     // wave-local row max (raw logits)
-    float mx = fmaxf(fmaxf(acc[0][0], acc[0][1]), fmaxf(acc[0][2], acc[0][3]));
+    // (a linear chain of three-input maxima: two new logits per instruction)
+    float mx = fmaxf(fmaxf(acc[0][0], acc[0][1]), acc[0][2]);
+    mx = fmaxf(fmaxf(mx, acc[0][3]), acc[1][0]);
 #pragma unroll
-    for (int t = 1; t < KTW; ++t) mx = fmaxf(mx, fmaxf(fmaxf(acc[t][0], acc[t][1]), fmaxf(acc[t][2], acc[t][3])));
+    for (int i = 5; i + 1 < 4 * KTW; i += 2) mx = fmaxf(fmaxf(mx, acc[i >> 2][i & 3]), acc[(i + 1) >> 2][(i + 1) & 3]);
+    mx = fmaxf(mx, acc[KTW - 1][3]);
     mx = group_max(mx);
-    const float moff = MASK && mx == -INFINITY ? 0.f : -mx * alpha;
+    const float ma = mx * alpha;                 // row max in base-2 exponent units
+    const float moff = MASK && mx == -INFINITY ? 0.f : -ma;
     float sp[4] = {0.f, 0.f, 0.f, 0.f};          // four partial sums: short dependency chains
 #pragma unroll
     for (int t = 0; t < KTW; ++t)
@@ -148,22 +161,17 @@ __device__ __forceinline__ void fused_unit(const Geo& g, int unit, const __bf16*
         sp[r] += e;
       }
     const float sm = group_sum((sp[0] + sp[1]) + (sp[2] + sp[3]));
-    if (lane < 16) red[buf][qlane][wave] = make_float2(mx, sm);
+    if (lane < 16) red[buf][qlane][wave] = make_float2(ma, sm);
     // publish tile b+1 before the barrier that ends this block's reads
     q_stash(buf ^ 1, cur);
     __syncthreads();
-    float m = -INFINITY;
-    float2 pr[FW];
-#pragma unroll
-    for (int w = 0; w < FW; ++w) {
-      pr[w] = red[buf][qlane][w];
-      m = fmaxf(m, pr[w].x);
-    }
-    float l = 0.f;
-#pragma unroll
-    for (int w = 0; w < FW; ++w) l += pr[w].y * fast_exp2((pr[w].x - m) * alpha);   // m_w = -inf -> 0
+    // lane group grp merges the pairs of waves 2 grp and 2 grp + 1; two lane
+    // swaps then combine the four groups (every lane ends with the row's m, l)
+    const float4 pp = *reinterpret_cast<const float4*>(&red[buf][qlane][2 * grp]);
+    const float m = group_max(fmaxf(pp.x, pp.z));
+    const float l = group_sum(pp.y * fast_exp2(pp.x - m) + pp.w * fast_exp2(pp.z - m));   // m_w = -inf -> 0
     // this wave's weight; rows past G*W contribute nothing
-    const float own = MASK && mx == -INFINITY ? 0.f : fast_exp2((mx - m) * alpha);
+    const float own = MASK && mx == -INFINITY ? 0.f : fast_exp2(ma - m);
     const float wgt = (b * QB + qlane < g.GW) ? own * __builtin_amdgcn_rcpf(l) : 0.f;
 #pragma unroll
     for (int t = 0; t < KTW; ++t)
