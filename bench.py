@@ -171,6 +171,9 @@ def main():
     k_save = wl.k_pool.index_select(1, blk_idx)
     v_save = wl.v_pool.index_select(1, blk_idx)
     tables_save = wl.block_tables.clone()
+    # everything above ran on the default stream; the bench stream must not
+    # start (restores read these copies) before it has finished
+    torch.cuda.synchronize()
 
     st = torch.cuda.Stream(device=dev)
     def restore():
@@ -238,6 +241,7 @@ def main():
     fused = None
     if K.kara_compress_fused_supported(cfg):
         done = torch.zeros(S, dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()                   # the counters are zero before the bench stream reads them
 
         def fused_step():
             K.kara_compress_fused(cfg, wl.q, wl.k_pool, wl.v_pool, wl.block_tables, wl.prior_lens, scores, kept,
@@ -264,6 +268,7 @@ def main():
     if a.consumer_reps > 0:
         from decode_kv_cache_amd.workloads import decode_queries
         q_dec = decode_queries(shape, dev)
+        torch.cuda.synchronize()                   # drawn on the default stream, read on the bench stream
         att = torch.empty((S, Lyr, shape.num_q_heads, d), dtype=torch.float32, device=dev)
         aws = torch.empty(K.kara_decode_attention_workspace_bytes(cfg) // 4 + 64, dtype=torch.float32, device=dev)
 
@@ -306,6 +311,14 @@ def main():
         log(f"[bench] achievable peaks: {achievable}")
         roof["frac_of_achievable"] = round(roof["achieved"] / achievable["mfma_bf16_tflops"], 4) \
             if shape.dtype == "bf16" else None
+        # the softmax around the MFMA: per logit one v_exp_f32 and four full-rate
+        # fp32 VALU operations (scale-and-shift, row sum, column update, max)
+        logits = float(G) * W * W * shape.units
+        floor_s = logits * (4.0 / achievable["fma_f32_per_s"] + 1.0 / achievable["v_exp_f32_per_s"])
+        roof["alu_floor"] = {"bound": "alu", "floor_ms": round(floor_s * 1e3, 3),
+                             "frac": round(floor_s / t_s, 4),
+                             "basis": "G*W^2 logits per unit x (4 fp32 VALU ops at the probed FMA rate + 1 "
+                                      "v_exp_f32 at the probed exp rate); packed fp32 is not used"}
         compact_roof["frac_of_achievable"] = round(compact_roof["achieved"] /
                                                    achievable["hbm_copy_GBps_read_plus_write"], 4)
         if consumer:

@@ -6,7 +6,7 @@
 //                      (32768 FLOP per wave per MFMA), accumulators independent
 //   kara_probe_exp   : blocks x 256 lanes, each iters x 8 v_exp_f32
 //   kara_probe_fma   : blocks x 256 lanes, each iters x 8 v_fma_f32
-//   kara_probe_read  : reads `bytes` once (16-byte non-temporal loads, 8 in
+//   kara_probe_read  : reads `bytes` once (16-byte non-temporal loads, 16 in
 //                      flight per thread) and writes one float per thread
 //   kara_probe_copy  : copies `bytes` (reads and writes each byte once)
 // Work sizes must keep every index inside the buffers: bytes a multiple of
@@ -16,7 +16,7 @@
 
 #include "kara_probes.h"
 
-namespace {
+namespace kara_probes {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -52,18 +52,24 @@ __global__ __launch_bounds__(256) void probe_valu(float* out, int iters, float a
   out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// Each workgroup streams whole 64 KiB chunks (16 loads of 16 bytes in flight
+// per thread, a wave covering 1 KiB per load), chunks handed out grid-stride.
 __global__ __launch_bounds__(256) void probe_read(const u32x4* __restrict__ src, size_t n, float* out) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  constexpr int PER = 16;                                  // loads in flight per thread
+  const size_t chunk = (size_t)256 * PER;                  // 16-byte elements per chunk
+  const size_t nchunks = n / chunk;
   unsigned acc = 0;
-  for (; i + 7 * stride < n; i += 8 * stride) {
-    u32x4 v[8];
+  for (size_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+    const u32x4* p = src + c * chunk + threadIdx.x;
+    u32x4 v[PER];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = __builtin_nontemporal_load(src + i + k * stride);
+    for (int k = 0; k < PER; ++k) v[k] = __builtin_nontemporal_load(p + k * 256);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+    for (int k = 0; k < PER; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
   }
-  for (; i < n; i += stride) acc ^= __builtin_nontemporal_load(src + i).x;
+  for (size_t i = nchunks * chunk + blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    acc ^= __builtin_nontemporal_load(src + i).x;
   out[blockIdx.x * blockDim.x + threadIdx.x] = (float)(acc & 1u);
 }
 
@@ -79,9 +85,11 @@ __global__ __launch_bounds__(256) void probe_copy(const u32x4* __restrict__ src,
   for (; i < n; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
-int status(hipError_t e) { return e == hipSuccess ? 0 : (int)e; }
+static int status(hipError_t e) { return e == hipSuccess ? 0 : (int)e; }
 
-}  // namespace
+}  // namespace kara_probes
+
+using namespace kara_probes;
 
 extern "C" {
 

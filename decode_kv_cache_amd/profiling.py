@@ -43,11 +43,45 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+_TYPES = {"DF16b": "__bf16", "f": "float", "d": "double", "i": "int"}
+
+
+def _demangle_kara(name: str) -> str:
+    """Readable form of the simple mangled names of this library's kernels
+    (namespace kara, optional template arguments of types and integers)."""
+    import re
+    m = re.match(r"_ZN4kara(?:12_GLOBAL__N_1)?(\d+)", name)
+    if not m:
+        return name
+    n = int(m.group(1))
+    ident = name[m.end():m.end() + n]
+    rest = name[m.end() + n:]
+    if rest.startswith("I"):
+        args, i = [], 1
+        while i < len(rest) and rest[i] != "E":
+            if rest.startswith("Li", i):
+                j = rest.index("E", i)
+                args.append(rest[i + 2:j])
+                i = j + 1
+                continue
+            for code, tname in _TYPES.items():
+                if rest.startswith(code, i):
+                    args.append(tname)
+                    i += len(code)
+                    break
+            else:
+                break
+        ident += "<" + ", ".join(args) + ">"
+    return ident
+
+
 def short_name(name: str) -> str:
+    if name.startswith("_Z"):
+        return _demangle_kara(name)
     s = name.replace("void ", "").split("(")[0]
     for pre in ("kara::(anonymous namespace)::", "kara::"):
         s = s.replace(pre, "")
-    return s.strip()
+    return s.strip() or "(unnamed probe kernel)"
 
 
 def _files(d, pattern):
@@ -117,11 +151,12 @@ def achievable_peaks(device=0) -> dict:
     t = timed(lambda: lib.kara_probe_fma(o, blocks, iters, sptr))
     fmas = blocks * 256 * iters * 8.0 / t
     nbytes = 4 << 30
-    grid = cus * 64
+    grid = cus * 8
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     sink = torch.empty(grid * 256, dtype=torch.float32, device=dev)
     sp, dp, kp = (ctypes.c_void_p(x.data_ptr()) for x in (src, dst, sink))
+    torch.cuda.synchronize(dev)                    # filled on the default stream, read on the probe stream
     t = timed(lambda: lib.kara_probe_read(sp, nbytes, kp, grid, sptr))
     read = nbytes / t / 1e9
     t = timed(lambda: lib.kara_probe_copy(sp, dp, nbytes, grid, sptr))
@@ -131,7 +166,8 @@ def achievable_peaks(device=0) -> dict:
             "fma_f32_per_s": float(f"{fmas:.4g}"), "hbm_read_GBps": round(read, 1),
             "hbm_copy_GBps_read_plus_write": round(copy, 1),
             "how": "libkara_probes.so: MFMA 32x32x16 bf16 loop, v_exp_f32 / v_fma_f32 chains (8 per lane per "
-                   "iteration), 4 GiB non-temporal read and copy; HIP events over 3 launches after one warm-up"}
+                   "iteration), 4 GiB non-temporal read (64 KiB chunks per workgroup) and copy; HIP events over "
+                   "3 launches after one warm-up"}
 
 
 def cmd_peaks(a):

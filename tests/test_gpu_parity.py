@@ -112,6 +112,7 @@ def test_repeat_runs_are_bit_identical_and_stream_ordered():
     for _ in range(2):
         wl = make_workload(s, "cuda")
         st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())    # the workload was written on the default stream
         with torch.cuda.stream(st):
             cfg, out = run_step(wl, stream=st)
         res.append((out["scores"].cpu(), out["kept"].cpu(), bits(wl.k_pool), bits(wl.v_pool),
