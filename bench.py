@@ -196,6 +196,22 @@ def main():
         if e:
             e[3].record(st)
 
+    def tables_match(upto_budget):
+        """Device block tables equal the workload's host copy over every
+        sequence's window blocks (after a restore) or over the blocks that
+        hold only kept slots (after a step)."""
+        got = wl.block_tables.cpu().numpy()
+        for n in range(S):
+            L = int(wl.host_prior_lens[n])
+            upto = (L + B) // bs if upto_budget else -(-(L + W) // bs)
+            if not np.array_equal(got[n, :upto], wl.host_tables[n, :upto]):
+                return False
+        return True
+
+    restore()
+    torch.cuda.synchronize()
+    if not tables_match(False):
+        sys.exit("bench: block tables differ from the workload after a restore")
     for _ in range(a.warmup):
         restore()
         step()
@@ -209,6 +225,8 @@ def main():
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    if not tables_match(True):
+        sys.exit("bench: block tables of the kept slots changed during the timed steps")
     t_score = [e[0].elapsed_time(e[1]) for e in events]
     t_sel = [e[1].elapsed_time(e[2]) for e in events]
     t_cmp = [e[2].elapsed_time(e[3]) for e in events]
