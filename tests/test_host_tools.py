@@ -1,0 +1,57 @@
+"""Host-side tooling: bench refuses more than one GPU, kernel-name demangling
+and the rocprofv3 CSV summaries used for the traffic figures."""
+import json
+import os
+import subprocess
+import sys
+
+from decode_kv_cache_amd import profiling
+from tests.conftest import ROOT
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
+
+
+def test_kernel_names_are_demangled():
+    f = profiling.short_name
+    assert f("_ZN4kara18decode_attn_kernelIDF16bLi128ELi4EEEvNS_7AttnGeoEPKT_") == "decode_attn_kernel<__bf16, 128, 4>"
+    assert f("_ZN4kara15pipeline_kernelENS_3GeoEPKDF16bPh") == "pipeline_kernel"
+    assert f("void kara::fused_score_kernel(kara::Geo, __bf16 const*)") == "fused_score_kernel"
+    assert f("compact_kernel<256>") == "compact_kernel<256>"
+
+
+def _csv(path, rows):
+    with open(path, "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for r in rows:
+            f.write(",".join(str(x) for x in r) + "\n")
+
+
+def test_traffic_scales_by_the_copy_calibration(tmp_path, monkeypatch):
+    for d in ("f", "w", "cf", "cw"):
+        (tmp_path / d).mkdir()
+    # two dispatches of the scorer, each split over two counter rows
+    _csv(tmp_path / "f" / "run_counter_collection.csv",
+         [(1, "void kara::fused_score_kernel(kara::Geo)", "FETCH_SIZE", 300), (1, "void kara::fused_score_kernel(kara::Geo)", "FETCH_SIZE", 200),
+          (2, "void kara::fused_score_kernel(kara::Geo)", "FETCH_SIZE", 500)])
+    _csv(tmp_path / "w" / "run_counter_collection.csv",
+         [(1, "void kara::fused_score_kernel(kara::Geo)", "WRITE_SIZE", 10), (2, "void kara::fused_score_kernel(kara::Geo)", "WRITE_SIZE", 30)])
+    _csv(tmp_path / "cf" / "run_counter_collection.csv", [(1, "at::native::neg_kernel", "FETCH_SIZE", 1024)])
+    _csv(tmp_path / "cw" / "run_counter_collection.csv", [(1, "at::native::neg_kernel", "WRITE_SIZE", 2048)])
+    assert profiling.counter_means(str(tmp_path / "f"), "FETCH_SIZE") == {"fused_score_kernel": 500.0}
+    monkeypatch.setattr(profiling, "ROOT", str(tmp_path))
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "decode_kv_cache_amd" / "csrc").mkdir(parents=True)
+    (tmp_path / "decode_kv_cache_amd" / "csrc" / "k.hip").write_text("x")
+    profiling.main(["traffic", "--workload", "w", "--fetch", str(tmp_path / "f"), "--write", str(tmp_path / "w"),
+                    "--copy-fetch", str(tmp_path / "cf"), "--copy-write", str(tmp_path / "cw"), "--copy-mib", "2"])
+    rec = json.loads((tmp_path / "profiles" / "traffic.json").read_text())["w"]
+    # copy of 2 MiB = 2048 KiB: FETCH reads 0.5x, WRITE 1.0x
+    assert abs(rec["copy_factor_fetch"] - 0.5) < 1e-12 and abs(rec["copy_factor_write"] - 1.0) < 1e-12
+    k = rec["kernels"]["fused_score_kernel"]
+    assert k["fetch_bytes"] == 500 * 1024 / 0.5 and k["write_bytes"] == 20 * 1024
+    assert rec["score_bytes_per_launch"] == k["bytes"]
