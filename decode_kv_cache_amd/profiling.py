@@ -7,6 +7,9 @@
     python -m decode_kv_cache_amd.profiling peaks
         achievable peaks on this GPU from libkara_probes.so (MFMA bf16 loop,
         v_exp_f32 and fp32 FMA rates, HBM read and copy bandwidth), as JSON;
+    python -m decode_kv_cache_amd.profiling counters <rocprofv3 --pmc output dirs>
+        per-kernel means of every collected counter, with MFMA busy and VALU
+        issue shares per SIMD;
     python -m decode_kv_cache_amd.profiling stats <rocprofv3 output dir>
         markdown table of per-kernel dispatch counts and durations;
     python -m decode_kv_cache_amd.profiling traffic --workload W --fetch D1 --write D2 \\
@@ -174,6 +177,46 @@ def cmd_peaks(a):
     print(json.dumps(achievable_peaks()), flush=True)
 
 
+def cmd_counters(a):
+    """Mean per dispatch of every counter found in the given rocprofv3 --pmc
+    output directories, for this library's kernels, with the derived
+    utilisations (SQ counters are totals over the chip's 1024 SIMDs; GRBM
+    counters over its 8 XCDs)."""
+    per = collections.defaultdict(lambda: collections.defaultdict(lambda: collections.defaultdict(float)))
+    for d in a.dirs:
+        for f in _files(d, "*counter_collection.csv"):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    k = short_name(r.get("Kernel_Name", ""))
+                    per[k][r["Counter_Name"]][(d, r.get("Dispatch_Id"))] += float(r["Counter_Value"])
+    for k in sorted(per):
+        if not any(t in k for t in ("score", "select", "compact", "finalize", "decode_attn", "pipeline", "row_lse",
+                                    "col_mass")):
+            continue
+        c = {name: sum(v.values()) / len(v) for name, v in per[k].items()}
+        print(f"### {k}")
+        print()
+        print("| Counter | Mean per dispatch |")
+        print("|---|---|")
+        for name in sorted(c):
+            print(f"| {name} | {c[name]:.4g} |")
+        simds, xcds = 1024.0, 8.0
+        if "GRBM_GUI_ACTIVE" in c:
+            cyc = c["GRBM_GUI_ACTIVE"] / xcds
+            print(f"| kernel cycles (GRBM_GUI_ACTIVE / 8 XCDs) | {cyc:.4g} |")
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                print(f"| MFMA busy per SIMD (SQ_VALU_MFMA_BUSY_CYCLES / 1024 / cycles) | "
+                      f"{c['SQ_VALU_MFMA_BUSY_CYCLES'] / simds / cyc:.3f} |")
+            if "SQ_INSTS_VALU" in c and "SQ_INSTS_VALU_TRANS_F32" in c:
+                # a wave64 VALU instruction holds a 16-lane SIMD for 4 cycles, a
+                # transcendental one (quarter rate) for 16
+                tr = c["SQ_INSTS_VALU_TRANS_F32"]
+                busy = ((c["SQ_INSTS_VALU"] - tr) * 4 + tr * 16) / simds / cyc
+                print(f"| VALU busy per SIMD ((SQ_INSTS_VALU - TRANS) x 4 + TRANS x 16 cycles / 1024 / cycles) | "
+                      f"{busy:.3f} |")
+        print()
+
+
 def cmd_copy(a):
     import torch
     n = a.mib * 1024 * 1024 // 4
@@ -235,6 +278,8 @@ def main(argv=None):
     c.add_argument("--mib", type=int, default=2048)
     c.add_argument("--reps", type=int, default=3)
     sub.add_parser("peaks")
+    cn = sub.add_parser("counters")
+    cn.add_argument("dirs", nargs="+")
     s = sub.add_parser("stats")
     s.add_argument("dir")
     t = sub.add_parser("traffic")
@@ -245,7 +290,8 @@ def main(argv=None):
     t.add_argument("--copy-write", required=True)
     t.add_argument("--copy-mib", type=int, required=True)
     a = p.parse_args(argv)
-    {"copy": cmd_copy, "peaks": cmd_peaks, "stats": cmd_stats, "traffic": cmd_traffic}[a.cmd](a)
+    {"copy": cmd_copy, "peaks": cmd_peaks, "stats": cmd_stats, "traffic": cmd_traffic,
+     "counters": cmd_counters}[a.cmd](a)
 
 
 if __name__ == "__main__":
