@@ -14,6 +14,9 @@ reasoning-model decode workloads the Kara pages describe):
 * Q, K, V entries are i.i.d. N(0, 1) unless the shape says otherwise;
 * ``key_model="outliers"``: per (layer, kv head) four key channels, drawn
   without replacement and shared by every token and sequence, are scaled x8;
+* ``key_model="spiky"``: N(0, 1) keys scaled x16, so logits span about
+  +-100 in base-2 exponent units and every softmax row is sharply peaked (a
+  numerical-range stress case, not a model of real keys);
 * ``key_model="student_t3"``: key entries are Student-t with 3 degrees of
   freedom, unscaled (z / sqrt(chi2_3 / 3));
 * ``plants=True``: per (sequence, layer, kv head) a unit direction u and six
@@ -69,7 +72,7 @@ class KaraShape:
     block_size: int = 16
     dtype: str = "bf16"                     # "bf16" or "f32" (Q, K and V share it)
     prior: tuple = ("fixed", 0)             # ("fixed", L) or ("uniform", lo, hi) inclusive
-    key_model: str = "normal"               # "normal" | "outliers" | "student_t3"
+    key_model: str = "normal"               # "normal" | "outliers" | "student_t3" | "spiky"
     plants: bool = False
     description: str = ""
 
@@ -254,6 +257,8 @@ def make_workload(shape: KaraShape, device="cpu", *, canary=True) -> Workload:
                 kn = torch.randn((W, Hkv, d), generator=gk, device=device, dtype=torch.float32)
             if shape.key_model == "outliers":
                 kn = kn * out_scale[l][None, :, :]
+            if shape.key_model == "spiky":
+                kn = kn * 16.0
             vn = torch.randn((W, Hkv, d), generator=_torch_gen(device, shape.shape_id, n, l, _TAG_V),
                              device=device, dtype=torch.float32)
             if shape.plants:

@@ -41,6 +41,11 @@ SMALL = [
     KaraShape("w4096_t3", 110, num_seqs=1, num_layers=1, num_q_heads=8, num_kv_heads=1, head_dim=128,
               window=4096, budget=820, seeds=24, radius=8, prior=("fixed", 32768), key_model="student_t3",
               plants=True),
+    # logits spanning about +-100 exponent units: sharply peaked rows, scores down to the fp32 range
+    KaraShape("spiky_fused", 113, num_seqs=2, num_layers=1, num_q_heads=8, num_kv_heads=2, head_dim=128,
+              window=512, budget=100, seeds=4, radius=3, prior=("fixed", 40), key_model="spiky"),
+    KaraShape("spiky_two_pass", 114, num_seqs=1, num_layers=1, num_q_heads=4, num_kv_heads=1, head_dim=64,
+              window=1500, budget=300, seeds=6, radius=4, prior=("fixed", 7), key_model="spiky"),
 ]
 
 
