@@ -282,6 +282,28 @@ def main():
                  "vs_three_calls": round(ms_step / ms_fused, 4)}
         log(f"[bench] one-launch pipeline {ms_fused:.3f} ms/step ({ms_step / ms_fused:.3f}x the three calls)")
 
+    # the bridging variant of the selection (largest gap the budget admits, up to 16)
+    bridged = None
+    gap = max([g_ for g_ in range(0, 17) if 0 <= K.kara_chunk_bound(cfg, g_) <= B], default=0)
+    if shape.seeds > 1 and gap > 0:
+        kept_b = torch.empty_like(kept)
+
+        def sel_ms(fn, reps=10):
+            fn()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(st)
+            for _ in range(reps):
+                fn()
+            ev[1].record(st)
+            torch.cuda.synchronize()
+            return ev[0].elapsed_time(ev[1]) / reps
+
+        t_plain = sel_ms(lambda: K.kara_select_chunks(cfg, scores, kept_b, None, st))
+        t_bridge = sel_ms(lambda: K.kara_select_chunks_bridged(cfg, gap, scores, kept_b, None, st))
+        bridged = {"call": "kara_select_chunks_bridged", "gap": gap, "ms": round(t_bridge, 4),
+                   "ms_plain_select": round(t_plain, 4)}
+        log(f"[bench] bridged selection (gap {gap}) {t_bridge:.3f} ms, plain {t_plain:.3f} ms")
+
     consumer = None
     if a.consumer_reps > 0:
         from decode_kv_cache_amd.workloads import decode_queries
@@ -363,6 +385,7 @@ def main():
         "roofline": roof,
         "compact_roofline": compact_roof,
         "fused_pipeline": fused,
+        "select_bridged": bridged,
         "decode_attention": consumer,
         "cpu_baseline": cpu,
         "achievable_peaks": achievable,

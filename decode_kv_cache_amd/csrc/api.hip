@@ -45,6 +45,8 @@ int check(const kara_config* c) {
   if (c->num_seqs > 0 && c->num_blocks < 1) return KARA_EINVAL;   // a window needs at least one block
   if (c->num_blocks > 0x7fffffffLL) return KARA_EINVAL;            // block ids are int32
   if ((long long)c->window > (long long)c->max_blocks_per_seq * c->block_size) return KARA_EINVAL;
+  // logical positions, and positions plus a step or a split, stay inside int32
+  if ((long long)c->max_blocks_per_seq * c->block_size > (1LL << 30)) return KARA_EINVAL;
   const long long units = (long long)c->num_seqs * c->num_layers * c->num_kv_heads;
   if (units > 0x3fffffffLL) return KARA_EINVAL;
   return KARA_OK;

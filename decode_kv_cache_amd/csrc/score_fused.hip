@@ -11,9 +11,11 @@
 // wave computes the 16 x 128 logits of its keys with 16x16x32 MFMAs in the
 // transposed orientation S^T = K Q^T, so a lane owns one query row and 32 of
 // the wave's keys:
-//   - row max and row sum are lane-local, then merged over the 4 lane groups
-//     that share a row (two lane swaps) and over the 8 waves (LDS, one
-//     barrier per block);
+//   - the row max is lane-local, then merged over the 4 lane groups that
+//     share a row (two lane swaps); the row sum of the wave's exponentials is
+//     a product with an all-ones matrix on the matrix cores (fp16 terms, fp32
+//     sum), which also spans the 4 lane groups; both are merged over the 8
+//     waves through LDS, one barrier per block;
 //   - every logit's softmax weight is a per-lane scalar times its
 //     exponential, and the column sums accumulate lane-locally across all
 //     blocks of the unit; they are reduced over the 16 query lanes once, at
@@ -26,6 +28,7 @@
 namespace kara {
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int FW = 8;            // waves per workgroup
 constexpr int FTHREADS = FW * 64;
@@ -105,6 +108,9 @@ __device__ __forceinline__ void fused_unit(const Geo& g, int unit, const __bf16*
   f32x4v colacc[KTW];
 #pragma unroll
   for (int t = 0; t < KTW; ++t) colacc[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
+  f16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.f;
 
   q_stash(0, q_fetch(0));
   uint2 stage1 = q_fetch(min(1, nblk - 1));    // tile b+1
@@ -151,16 +157,25 @@ __device__ __forceinline__ void fused_unit(const Geo& g, int unit, const __bf16*
     mx = group_max(mx);
     const float ma = mx * alpha;                 // row max in base-2 exponent units
     const float moff = MASK && mx == -INFINITY ? 0.f : -ma;
-    float sp[4] = {0.f, 0.f, 0.f, 0.f};          // four partial sums: short dependency chains
+    // The wave's row sum runs on the matrix cores: the exponentials of two
+    // tiles (8 per lane, all of row qlane) are rounded to fp16 and form the B
+    // operand of a product with an all-ones A, so every lane receives the sum
+    // over the 32 keys of the four lane groups, accumulated in fp32.
+    f32x4v rs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < KTW; ++t)
+    for (int t = 0; t < KTW; t += 2) {
+      f16x8 h;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float e = fast_exp2(__builtin_fmaf(acc[t][r], alpha, moff));
-        acc[t][r] = e;
-        sp[r] += e;
-      }
-    const float sm = group_sum((sp[0] + sp[1]) + (sp[2] + sp[3]));
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = fast_exp2(__builtin_fmaf(acc[t + u][r], alpha, moff));
+          acc[t + u][r] = e;
+          h[4 * u + r] = (_Float16)e;
+        }
+      rs = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, h, rs, 0, 0, 0);
+    }
+    const float sm = rs[0];
     if (lane < 16) red[buf][qlane][wave] = make_float2(ma, sm);
     // publish tile b+1 before the barrier that ends this block's reads
     q_stash(buf ^ 1, cur);

@@ -81,7 +81,7 @@ typedef struct kara_config {
   int32_t radius;        /* r >= 0, with s*(2r+1) <= B */
   int32_t block_size;    /* power of two, 1..256 */
   int32_t dtype;         /* KARA_BF16 or KARA_F32 */
-  int32_t max_blocks_per_seq; /* >= 1, columns of block_tables */
+  int32_t max_blocks_per_seq; /* >= 1, columns of block_tables; times block_size at most 2^30 */
   int64_t num_blocks;    /* physical blocks per layer in k_cache / v_cache: 0..2^31-1, >= 1 if num_seqs > 0 */
 } kara_config;
 

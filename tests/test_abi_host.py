@@ -55,9 +55,15 @@ def test_all_benchmark_shapes_are_valid():
     ("head_dim", 96), ("head_dim", 256), ("window", 0), ("window", 8193), ("budget", 0), ("budget", 1025),
     ("seeds", -1), ("radius", -1), ("seeds", 20), ("block_size", 12), ("block_size", 512), ("dtype", 7),
     ("max_blocks_per_seq", 0), ("num_blocks", -1), ("max_blocks_per_seq", 63),
+    ("max_blocks_per_seq", 2 ** 30 // 16 + 1),      # more than 2^30 logical slots at block size 16
 ])
 def test_invalid_config_fields(field, value):
     assert K.kara_check_config(_cfg(**{field: value})) == -1
+
+
+def test_logical_positions_fit_int32():
+    assert K.kara_check_config(_cfg(max_blocks_per_seq=2 ** 30 // 16)) == 0
+    assert K.kara_check_config(_cfg(max_blocks_per_seq=2 ** 30 // 16 + 1)) == -1
 
 
 def test_seed_span_constraint_is_exact():
