@@ -359,8 +359,8 @@ def main():
                              "frac": round(floor_s / t_s, 4),
                              "basis": "G*W^2 logits per unit x (4 fp32 VALU ops at the probed FMA rate + 1 "
                                       "v_exp_f32 at the probed exp rate); packed fp32 is not used"}
-        compact_roof["frac_of_achievable"] = round(compact_roof["achieved"] /
-                                                   achievable["hbm_copy_GBps_read_plus_write"], 4)
+        compact_roof["frac_of_achievable"] = round(compact_roof["achieved"] / max(
+            achievable["hbm_copy_GBps_read_plus_write"], achievable["hbm_rewrite_in_place_GBps_read_plus_write"]), 4)
         if consumer:
             consumer["roofline"]["frac_of_achievable"] = round(consumer["roofline"]["achieved"] /
                                                                achievable["hbm_read_GBps"], 4)

@@ -1,4 +1,4 @@
-// Compaction kernels: one workgroup per (unit, K-or-V) copies the kept rows
+// Compaction kernels: one workgroup per unit copies the kept K and V rows
 // into place (compact_core.h), then one thread per sequence rewrites its
 // block table.  Kara's English abstract: the method is adapted to
 // PagedAttention and lowers KV-cache memory.
@@ -7,7 +7,10 @@
 namespace kara {
 
 constexpr int CMP_THREADS = 256;
-constexpr int CMP_VEC = 16;  // 16-byte vectors per thread per chunk (256 rows of 256 B)
+// 16-byte vectors per thread and pool per chunk: 80 rows of 256 B per chunk,
+// 10 loads in flight per thread; a small register footprint keeps many
+// workgroups resident, which is what sustains the bandwidth
+constexpr int CMP_VEC = 5;
 
 template <int ROWBYTES>
 __global__ __launch_bounds__(CMP_THREADS) void compact_kernel(Geo g, unsigned char* __restrict__ kc,
@@ -15,12 +18,11 @@ __global__ __launch_bounds__(CMP_THREADS) void compact_kernel(Geo g, unsigned ch
                                                               const int32_t* __restrict__ tables,
                                                               const int32_t* __restrict__ prior,
                                                               const int32_t* __restrict__ kept, int esize) {
-  const long long unit = blockIdx.x >> 1;
-  unsigned char* pool = (blockIdx.x & 1) ? vc : kc;
+  const long long unit = blockIdx.x;
   const int kvh = (int)(unit % g.Hkv);
   const int layer = (int)((unit / g.Hkv) % g.Lyr);
   const int n = (int)(unit / ((long long)g.Hkv * g.Lyr));
-  compact_unit_rows<CMP_THREADS, ROWBYTES, CMP_VEC>(g, pool, tables + (long long)n * g.max_blocks, layer, kvh,
+  compact_unit_rows<CMP_THREADS, ROWBYTES, CMP_VEC>(g, kc, vc, tables + (long long)n * g.max_blocks, layer, kvh,
                                                    prior[n], kept + unit * g.B, esize);
 }
 
@@ -37,11 +39,11 @@ hipError_t launch_compact(const Geo& g, int dtype, void* kc, void* vc, int32_t* 
                           int32_t* seq_lens, const int32_t* kept, int32_t* freed, int32_t* num_freed,
                           int max_freed, hipStream_t st) {
   const long long units = (long long)g.S * g.Lyr * g.Hkv;
-  if (2 * units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const int esize = dtype == KARA_BF16 ? 2 : 4;
   const int rowbytes = g.D * esize;
   if (units > 0) {
-    const dim3 grid((unsigned)(2 * units));
+    const dim3 grid((unsigned)units);
     if (rowbytes == 128)
       hipLaunchKernelGGL(compact_kernel<128>, grid, dim3(CMP_THREADS), 0, st, g, (unsigned char*)kc,
                          (unsigned char*)vc, tables, prior, kept, esize);

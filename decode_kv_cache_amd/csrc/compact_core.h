@@ -23,10 +23,14 @@ namespace kara {
 // rows are streamed once: non-temporal loads and stores keep them out of the caches
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Copy the B kept rows of one (unit, pool) into place.  kl = the unit's kept
-// list (global or LDS); NT threads, VEC 16-byte vectors per thread per chunk.
+// Copy the B kept rows of one unit into place, in the K pool and the V pool
+// together: both use the same source and destination slots, so each row's
+// two table lookups serve both copies and the loads of both pools are in
+// flight at once.  kl = the unit's kept list (global or LDS); NT threads,
+// VEC 16-byte vectors per thread and pool per chunk.
 template <int NT, int ROWBYTES, int VEC>
-__device__ __forceinline__ void compact_unit_rows(const Geo& g, unsigned char* __restrict__ pool,
+__device__ __forceinline__ void compact_unit_rows(const Geo& g, unsigned char* __restrict__ kpool,
+                                                  unsigned char* __restrict__ vpool,
                                                   const int32_t* __restrict__ trow, int layer, int kvh, int L,
                                                   const int32_t* kl, int esize) {
   constexpr int TPR = ROWBYTES / 16;                  // threads per row
@@ -36,7 +40,7 @@ __device__ __forceinline__ void compact_unit_rows(const Geo& g, unsigned char* _
   const int part = t % TPR;
   const int rsub = t / TPR;
   for (int c0 = 0; c0 < g.B; c0 += CH) {
-    u32x4 buf[VEC];
+    u32x4 bk[VEC], bv[VEC];
     long long dst[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) {
@@ -47,8 +51,10 @@ __device__ __forceinline__ void compact_unit_rows(const Geo& g, unsigned char* _
         const long long so = (j >= 0 && j < g.W) ? slot_offset(g, trow, layer, kvh, L + j) : -1;
         const long long d = slot_offset(g, trow, layer, kvh, L + r);
         if (so >= 0 && d >= 0) {
-          buf[v] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pool + so * esize + part * 16));
-          dst[v] = d;
+          const long long o = so * esize + part * 16;
+          bk[v] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kpool + o));
+          bv[v] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vpool + o));
+          dst[v] = d * esize + part * 16;
         }
       }
     }
@@ -56,7 +62,10 @@ __device__ __forceinline__ void compact_unit_rows(const Geo& g, unsigned char* _
     __syncthreads();
 #pragma unroll
     for (int v = 0; v < VEC; ++v)
-      if (dst[v] >= 0) __builtin_nontemporal_store(buf[v], reinterpret_cast<u32x4*>(pool + dst[v] * esize + part * 16));
+      if (dst[v] >= 0) {
+        __builtin_nontemporal_store(bk[v], reinterpret_cast<u32x4*>(kpool + dst[v]));
+        __builtin_nontemporal_store(bv[v], reinterpret_cast<u32x4*>(vpool + dst[v]));
+      }
   }
 }
 

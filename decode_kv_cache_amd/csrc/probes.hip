@@ -9,6 +9,9 @@
 //   kara_probe_read  : reads `bytes` once (16-byte non-temporal loads, 16 in
 //                      flight per thread) and writes one float per thread
 //   kara_probe_copy  : copies `bytes` (reads and writes each byte once)
+//   kara_probe_rewrite: reads `bytes` and writes them back in place, one
+//                      workgroup per 16 KiB (the access shape of in-place
+//                      row compaction)
 // Work sizes must keep every index inside the buffers: bytes a multiple of
 // 16, out holding blocks * 256 floats (read: grid * 256 floats, grid given).
 #include <hip/hip_runtime.h>
@@ -85,6 +88,23 @@ __global__ __launch_bounds__(256) void probe_copy(const u32x4* __restrict__ src,
   for (; i < n; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
+// In-place rewrite: one short-lived workgroup per 16 KiB chunk, 4 loads of 16
+// bytes in flight per thread, then the same 4 vectors stored back where they
+// were read (each element is touched by one thread only).  Measured on
+// gfx950 over 4 and 16 GiB: 4 vectors per thread sustain the most, 8 fall
+// well behind.
+constexpr int RW_PER = 4;
+__global__ __launch_bounds__(256) void probe_rewrite(u32x4* buf, size_t n) {
+  const size_t base = (size_t)blockIdx.x * 256 * RW_PER + threadIdx.x;
+  u32x4 v[RW_PER];
+#pragma unroll
+  for (int k = 0; k < RW_PER; ++k)
+    if (base + k * 256 < n) v[k] = __builtin_nontemporal_load(buf + base + k * 256);
+#pragma unroll
+  for (int k = 0; k < RW_PER; ++k)
+    if (base + k * 256 < n) __builtin_nontemporal_store(v[k], buf + base + k * 256);
+}
+
 static int status(hipError_t e) { return e == hipSuccess ? 0 : (int)e; }
 
 }  // namespace kara_probes
@@ -121,6 +141,16 @@ int kara_probe_read(const void* src, size_t bytes, float* out, int grid, void* s
 int kara_probe_copy(const void* src, void* dst, size_t bytes, int grid, void* stream) {
   if (!src || !dst || grid < 1 || (bytes & 15)) return -1;
   hipLaunchKernelGGL(probe_copy, dim3(grid), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src, (u32x4*)dst,
+                     bytes / 16);
+  return status(hipGetLastError());
+}
+
+int kara_probe_rewrite(void* buf, size_t bytes, void* stream) {
+  if (!buf || (bytes & 15)) return -1;
+  const size_t chunks = (bytes / 16 + 256 * RW_PER - 1) / (256 * RW_PER);
+  if (chunks == 0) return 0;
+  if (chunks > 0x7fffffffULL) return -1;
+  hipLaunchKernelGGL(probe_rewrite, dim3((unsigned)chunks), dim3(256), 0, (hipStream_t)stream, (u32x4*)buf,
                      bytes / 16);
   return status(hipGetLastError());
 }

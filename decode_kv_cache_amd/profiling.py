@@ -37,10 +37,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def kernel_source_hash() -> str:
-    """Hash of every kernel source; a stored measurement is valid for it only."""
+    """Hash of every library kernel source (the probes are tools, not part of
+    it); a stored measurement is valid for this hash only."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "decode_kv_cache_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
+        if f == "probes.hip":
+            continue
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -125,7 +128,7 @@ def achievable_peaks(device=0) -> dict:
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     for name, args in (("kara_probe_mfma", [vp, i32, i32, vp]), ("kara_probe_exp", [vp, i32, i32, vp]),
                        ("kara_probe_fma", [vp, i32, i32, vp]), ("kara_probe_read", [vp, sz, vp, i32, vp]),
-                       ("kara_probe_copy", [vp, vp, sz, i32, vp])):
+                       ("kara_probe_copy", [vp, vp, sz, i32, vp]), ("kara_probe_rewrite", [vp, sz, vp])):
         getattr(lib, name).argtypes = args
         getattr(lib, name).restype = i32
     dev = torch.device("cuda", device)
@@ -164,12 +167,16 @@ def achievable_peaks(device=0) -> dict:
     read = nbytes / t / 1e9
     t = timed(lambda: lib.kara_probe_copy(sp, dp, nbytes, grid, sptr))
     copy = 2 * nbytes / t / 1e9
+    t = timed(lambda: lib.kara_probe_rewrite(dp, nbytes, sptr))
+    rewrite = 2 * nbytes / t / 1e9
     del src, dst
     return {"mfma_bf16_tflops": round(mfma, 1), "v_exp_f32_per_s": float(f"{exps:.4g}"),
             "fma_f32_per_s": float(f"{fmas:.4g}"), "hbm_read_GBps": round(read, 1),
             "hbm_copy_GBps_read_plus_write": round(copy, 1),
+            "hbm_rewrite_in_place_GBps_read_plus_write": round(rewrite, 1),
             "how": "libkara_probes.so: MFMA 32x32x16 bf16 loop, v_exp_f32 / v_fma_f32 chains (8 per lane per "
-                   "iteration), 4 GiB non-temporal read (64 KiB chunks per workgroup) and copy; HIP events over "
+                   "iteration), 4 GiB non-temporal read (64 KiB chunks per workgroup, grid-stride), copy "
+                   "(grid-stride) and in-place rewrite (one workgroup per 16 KiB); HIP events over "
                    "3 launches after one warm-up"}
 
 
@@ -271,6 +278,69 @@ def cmd_traffic(a):
         json.dump(data, f, indent=1)
 
 
+def cmd_compact_patterns(a):
+    """Time kara_compact_paged on one workload with several kept patterns: the
+    selection the step makes, and synthetic ones with the same budget (dense
+    in place, dense shifted, strided, uniformly random).  Only the block
+    tables are restored between launches; pool contents do not change the
+    work.  Rate = 2 pools x B rows x row bytes x (read + write) x units."""
+    import numpy as np
+    import torch
+
+    from decode_kv_cache_amd import kara as K
+    from decode_kv_cache_amd.workloads import make_workload, shape_by_name
+    shape = shape_by_name(a.workload)
+    wl = make_workload(shape, "cuda")
+    cfg = K.make_config(shape, max_blocks_per_seq=wl.max_blocks, num_blocks=wl.num_blocks)
+    S, Lyr, Hkv, W, B = shape.num_seqs, shape.num_layers, shape.num_kv_heads, shape.window, shape.budget
+    dev = wl.q.device
+    st = torch.cuda.Stream()
+    scores = torch.empty((S, Lyr, Hkv, W), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(K.kara_workspace_bytes(cfg) // 4, 1), dtype=torch.float32, device=dev)
+    sel = torch.empty((S, Lyr, Hkv, B), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    K.kara_score_window(cfg, wl.q, wl.k_pool, wl.block_tables, wl.prior_lens, scores, ws, st)
+    K.kara_select_chunks(cfg, scores, sel, None, st)
+    st.synchronize()
+    gen = np.random.default_rng(1234)
+    units = S * Lyr * Hkv
+    rnd = np.sort(np.argsort(gen.random((units, W)), axis=1)[:, :B], axis=1).astype(np.int32)
+    r = torch.arange(B, dtype=torch.int32, device=dev)
+    patterns = {
+        "selection made by the step": sel,
+        "dense in place (kept[r] = r)": r.expand(S, Lyr, Hkv, B).contiguous(),
+        "dense shifted (kept[r] = r + W - B)": (r + (W - B)).expand(S, Lyr, Hkv, B).contiguous(),
+        f"strided (kept[r] = {W // B} r)": (r * (W // B)).expand(S, Lyr, Hkv, B).contiguous(),
+        "uniform random subset": torch.from_numpy(rnd).to(dev).view(S, Lyr, Hkv, B),
+    }
+    tables0 = wl.block_tables.clone()
+    seq = torch.empty(S, dtype=torch.int32, device=dev)
+    freed = torch.empty((S, K.kara_max_freed(cfg)), dtype=torch.int32, device=dev)
+    nfreed = torch.empty(S, dtype=torch.int32, device=dev)
+    esize = 2 if shape.dtype == "bf16" else 4
+    nbytes = 2 * 2 * B * shape.head_dim * esize * units
+    torch.cuda.synchronize()
+    print(f"| Kept pattern ({a.workload}, {units} units, B = {B} of W = {W}) | ms per launch | GB/s |")
+    print("|---|---|---|")
+    for name, kept in patterns.items():
+        ts = []
+        for _ in range(a.reps + 1):
+            with torch.cuda.stream(st):
+                wl.block_tables.copy_(tables0)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(st)
+            K.kara_compact_paged(cfg, wl.k_pool, wl.v_pool, wl.block_tables, wl.prior_lens, seq, kept, freed,
+                                 nfreed, st)
+            ev[1].record(st)
+            st.synchronize()
+            ts.append(ev[0].elapsed_time(ev[1]))
+        ms = float(np.median(ts[1:]))
+        print(f"| {name} | {ms:.3f} | {nbytes / ms / 1e6:.0f} |", flush=True)
+    with torch.cuda.stream(st):
+        wl.block_tables.copy_(tables0)
+    st.synchronize()
+
+
 def main(argv=None):
     p = argparse.ArgumentParser(prog="python -m decode_kv_cache_amd.profiling")
     sub = p.add_subparsers(dest="cmd", required=True)
@@ -289,8 +359,11 @@ def main(argv=None):
     t.add_argument("--copy-fetch", required=True)
     t.add_argument("--copy-write", required=True)
     t.add_argument("--copy-mib", type=int, required=True)
+    cp = sub.add_parser("compact_patterns")
+    cp.add_argument("--workload", default="llama8b_b64")
+    cp.add_argument("--reps", type=int, default=5)
     a = p.parse_args(argv)
-    {"copy": cmd_copy, "peaks": cmd_peaks, "stats": cmd_stats, "traffic": cmd_traffic,
+    {"compact_patterns": cmd_compact_patterns, "copy": cmd_copy, "peaks": cmd_peaks, "stats": cmd_stats, "traffic": cmd_traffic,
      "counters": cmd_counters}[a.cmd](a)
 
 

@@ -28,8 +28,13 @@ int kara_probe_fma(float* out, int blocks, int iters, void* stream);
 /* Reads `bytes` (a multiple of 16) of src once.  out: grid * 256 floats. */
 int kara_probe_read(const void* src, size_t bytes, float* out, int grid, void* stream);
 
-/* Copies `bytes` (a multiple of 16) from src to dst (each byte read and written once). */
+/* Copies `bytes` (a multiple of 16) from src to dst (each byte read and written once).  grid
+ * workgroups of 256 threads stride over the buffer. */
 int kara_probe_copy(const void* src, void* dst, size_t bytes, int grid, void* stream);
+
+/* Reads `bytes` (a multiple of 16) of buf and writes them back in place (each byte read and
+ * written once), one workgroup per 16 KiB chunk. */
+int kara_probe_rewrite(void* buf, size_t bytes, void* stream);
 
 #ifdef __cplusplus
 }
