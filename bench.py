@@ -39,7 +39,7 @@ def log(msg):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="llama8b_b64")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the oracle sample")

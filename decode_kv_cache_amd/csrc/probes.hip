@@ -8,6 +8,9 @@
 //   kara_probe_fma   : blocks x 256 lanes, each iters x 8 v_fma_f32
 //   kara_probe_read  : reads `bytes` once (16-byte non-temporal loads, 16 in
 //                      flight per thread) and writes one float per thread
+//   kara_probe_coissue: MFMAs alone, fp32 FMAs alone, and both interleaved in
+//                      one instruction stream (4 MFMAs and 16 VALU operations
+//                      per iteration), to see how far they run concurrently
 //   kara_probe_copy  : copies `bytes` (reads and writes each byte once)
 //   kara_probe_rewrite: reads `bytes` and writes them back in place, one
 //                      workgroup per 16 KiB (the access shape of in-place
@@ -105,6 +108,38 @@ __global__ __launch_bounds__(256) void probe_rewrite(u32x4* buf, size_t n) {
     if (base + k * 256 < n) __builtin_nontemporal_store(v[k], buf + base + k * 256);
 }
 
+// MFMA / VALU co-issue: per iteration 4 independent 16x16x32 bf16 MFMAs
+// (MODE 0), 16 independent fp32 FMAs (MODE 1), both interleaved as MFMA, 4
+// FMAs, MFMA, ... (MODE 2), the MFMAs interleaved with 16 v_exp_f32 (MODE 3),
+// or the 16 v_exp_f32 alone (MODE 4).
+template <int MODE>
+__global__ __launch_bounds__(512) void probe_coissue(float* out, int iters, float a) {
+  bf16x8 x, y;
+  for (int i = 0; i < 8; ++i) {
+    x[i] = (__bf16)(threadIdx.x * 1e-3f);
+    y[i] = (__bf16)(i * 1e-3f);
+  }
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  f32x4 c[4] = {};
+  float v[16];
+  for (int e = 0; e < 16; ++e) v[e] = threadIdx.x * 1e-3f + e;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      if (MODE == 0 || MODE == 2 || MODE == 3) c[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, c[m], 0, 0, 0);
+      if (MODE != 0) {
+#pragma unroll
+        for (int e = 4 * m; e < 4 * m + 4; ++e)
+          v[e] = MODE >= 3 ? __builtin_amdgcn_exp2f(v[e] * a) : __builtin_fmaf(v[e], a, 0.5f);
+      }
+    }
+  }
+  float s = 0.f;
+  for (int m = 0; m < 4; ++m) s += c[m][0] + c[m][1] + c[m][2] + c[m][3];
+  for (int e = 0; e < 16; ++e) s += v[e];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 static int status(hipError_t e) { return e == hipSuccess ? 0 : (int)e; }
 
 }  // namespace kara_probes
@@ -142,6 +177,21 @@ int kara_probe_copy(const void* src, void* dst, size_t bytes, int grid, void* st
   if (!src || !dst || grid < 1 || (bytes & 15)) return -1;
   hipLaunchKernelGGL(probe_copy, dim3(grid), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src, (u32x4*)dst,
                      bytes / 16);
+  return status(hipGetLastError());
+}
+
+int kara_probe_coissue(int mode, float* out, int blocks, int threads, int iters, void* stream) {
+  if (!out || blocks < 1 || iters < 1 || threads < 64 || threads > 512 || threads % 64) return -1;
+  const dim3 g(blocks), b(threads);
+  const hipStream_t st = (hipStream_t)stream;
+  switch (mode) {
+    case 0: hipLaunchKernelGGL(probe_coissue<0>, g, b, 0, st, out, iters, 0.999f); break;
+    case 1: hipLaunchKernelGGL(probe_coissue<1>, g, b, 0, st, out, iters, 0.999f); break;
+    case 2: hipLaunchKernelGGL(probe_coissue<2>, g, b, 0, st, out, iters, 0.999f); break;
+    case 3: hipLaunchKernelGGL(probe_coissue<3>, g, b, 0, st, out, iters, 0.999f); break;
+    case 4: hipLaunchKernelGGL(probe_coissue<4>, g, b, 0, st, out, iters, 0.999f); break;
+    default: return -1;
+  }
   return status(hipGetLastError());
 }
 

@@ -278,6 +278,49 @@ def cmd_traffic(a):
         json.dump(data, f, indent=1)
 
 
+def cmd_coissue(a):
+    """Time kara_probe_coissue's four modes at 1, 2 and 4 waves per SIMD and
+    print ns per wave-iteration per SIMD, with the overlap of the MFMA and
+    VALU parts: (t_mfma + t_valu - t_both) / min(t_mfma, t_valu)."""
+    import ctypes
+
+    import torch
+    path = os.path.join(ROOT, "decode_kv_cache_amd", "libkara_probes.so")
+    lib = ctypes.CDLL(path)
+    lib.kara_probe_coissue.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_void_p]
+    lib.kara_probe_coissue.restype = ctypes.c_int
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    simds = 4 * cus
+    st = torch.cuda.Stream()
+    sp = ctypes.c_void_p(st.cuda_stream)
+    out = torch.empty(4 * cus * 512, dtype=torch.float32, device="cuda")
+    o = ctypes.c_void_p(out.data_ptr())
+    iters = a.iters
+
+    def ns(mode, blocks, threads):
+        f = lambda: lib.kara_probe_coissue(mode, o, blocks, threads, iters, sp)
+        if f() != 0:
+            raise RuntimeError("probe launch failed")
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(st)
+        f()
+        ev[1].record(st)
+        torch.cuda.synchronize()
+        waves_per_simd = blocks * threads / 64 / simds
+        return ev[0].elapsed_time(ev[1]) * 1e6 / iters / waves_per_simd
+
+    print("| Waves per SIMD | 4 MFMA | 16 FMA | 4 MFMA + 16 FMA | overlap | 16 v_exp_f32 | 4 MFMA + 16 v_exp_f32 "
+          "| overlap |")
+    print("|---|---|---|---|---|---|---|---|")
+    for label, blocks, threads in (("1", cus, 256), ("2", cus, 512), ("4", 4 * cus, 256)):
+        tm, tf, tb, tmx, tx = (ns(m, blocks, threads) for m in (0, 1, 2, 3, 4))
+        ov = (tm + tf - tb) / min(tm, tf)
+        ox = (tm + tx - tmx) / min(tm, tx)
+        print(f"| {label} | {tm:.1f} ns | {tf:.1f} ns | {tb:.1f} ns | {100 * ov:.0f} % | {tx:.1f} ns | {tmx:.1f} ns "
+              f"| {100 * ox:.0f} % |", flush=True)
+
+
 def cmd_compact_patterns(a):
     """Time kara_compact_paged on one workload with several kept patterns: the
     selection the step makes, and synthetic ones with the same budget (dense
@@ -359,11 +402,13 @@ def main(argv=None):
     t.add_argument("--copy-fetch", required=True)
     t.add_argument("--copy-write", required=True)
     t.add_argument("--copy-mib", type=int, required=True)
+    ci = sub.add_parser("coissue")
+    ci.add_argument("--iters", type=int, default=20000)
     cp = sub.add_parser("compact_patterns")
     cp.add_argument("--workload", default="llama8b_b64")
     cp.add_argument("--reps", type=int, default=5)
     a = p.parse_args(argv)
-    {"compact_patterns": cmd_compact_patterns, "copy": cmd_copy, "peaks": cmd_peaks, "stats": cmd_stats, "traffic": cmd_traffic,
+    {"coissue": cmd_coissue, "compact_patterns": cmd_compact_patterns, "copy": cmd_copy, "peaks": cmd_peaks, "stats": cmd_stats, "traffic": cmd_traffic,
      "counters": cmd_counters}[a.cmd](a)
 
 

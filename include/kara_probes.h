@@ -25,6 +25,14 @@ int kara_probe_exp(float* out, int blocks, int iters, void* stream);
 /* blocks x 256 lanes; each lane issues iters x 8 fp32 FMA.  out: blocks * 256 floats. */
 int kara_probe_fma(float* out, int blocks, int iters, void* stream);
 
+/* blocks x threads lanes (threads a multiple of 64, at most 512), iters iterations of:
+ * mode 0: 4 independent MFMA 16x16x32 bf16; mode 1: 16 independent fp32 FMA; mode 2: both,
+ * interleaved (MFMA, 4 FMA, MFMA, ...); mode 3: the MFMAs interleaved with 16 v_exp_f32;
+ * mode 4: the 16 v_exp_f32 alone.
+ * out: blocks * threads floats.  Comparing the modes' times shows how far the matrix cores
+ * and the VALU overlap at a given number of waves per SIMD. */
+int kara_probe_coissue(int mode, float* out, int blocks, int threads, int iters, void* stream);
+
 /* Reads `bytes` (a multiple of 16) of src once.  out: grid * 256 floats. */
 int kara_probe_read(const void* src, size_t bytes, float* out, int grid, void* stream);
 
