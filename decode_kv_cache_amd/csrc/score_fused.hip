@@ -334,7 +334,7 @@ __global__ __launch_bounds__(FTHREADS, 1) void pipeline_kernel(Geo g, const __bf
   select_unit<FTHREADS, FW * KTW * 16 / FTHREADS>(g, 0, keys, flags, sh, kl, kept + (long long)unit * g.B,
                         mask ? mask + (long long)unit * g.W : nullptr);
   __syncthreads();                                   // kl complete
-  compact_unit_rows<FTHREADS, FD * 2, 4>(g, kc, vc, trow, layer, kvh, L, kl, 2);
+  compact_unit_rows<FTHREADS, FD * 2, 8>(g, kc, vc, trow, layer, kvh, L, kl, 2);   // B <= 256 in one round
   __syncthreads();                                   // every table read of this workgroup is done
   if (tid == 0) {
     __threadfence();
