@@ -37,7 +37,8 @@ Readings taken where the pages are silent (each is stated where used):
   order; exactly ``budget`` positions are kept, listed in ascending order.
 * R20     bridging variant (not the main rule): neighbouring seeds that leave
   at most ``gap`` positions between them are joined by keeping everything in
-  between (the explainers' "keep what lies between two important points").
+  between (the lay explainers of KARA, part 2, describe keeping the tokens
+  that lie between two important ones).
 * R25/R26 the consumer (decode attention) reads every cached slot [0, seq_len)
   of the sequence through its block table, scale 1/sqrt(d), GQA as in R4; an
   empty cache yields a zero output.
