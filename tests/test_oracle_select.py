@@ -1,7 +1,7 @@
 """Pins of the oracle's Token2Chunk selection (a5-a8).
 
-Rule (reading R9-R13 of the Kara abstract's "expand a subset of selected KV
-pairs into chunks"): seeds = first s of the order (score desc, position asc),
+Rule (reading R9-R13 of the Kara abstract, where part of the selected KV
+pairs grows into chunks): seeds = first s of the order (score desc, position asc),
 spans [p-r, p+r] clipped and merged, fill = best positions outside the spans,
 exactly B kept, ascending.
 """
