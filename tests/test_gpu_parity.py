@@ -46,6 +46,16 @@ SMALL = [
               window=512, budget=100, seeds=4, radius=3, prior=("fixed", 40), key_model="spiky"),
     KaraShape("spiky_two_pass", 114, num_seqs=1, num_layers=1, num_q_heads=4, num_kv_heads=1, head_dim=64,
               window=1500, budget=300, seeds=6, radius=4, prior=("fixed", 7), key_model="spiky"),
+    # the largest window, the largest block size, and a budget of many seeded chunks
+    KaraShape("w8192_bs256", 115, num_seqs=1, num_layers=1, num_q_heads=2, num_kv_heads=1, head_dim=64,
+              window=8192, budget=1024, seeds=32, radius=15, prior=("fixed", 300), block_size=256,
+              key_model="student_t3", plants=True),
+    # the largest window kept whole: compaction moves nothing and frees nothing
+    KaraShape("w8192_keep_all", 116, num_seqs=1, num_layers=1, num_q_heads=1, num_kv_heads=1, head_dim=64,
+              window=8192, budget=8192, seeds=1, radius=0, prior=("fixed", 21), block_size=128, dtype="f32"),
+    # sixteen query heads per KV head
+    KaraShape("g16", 117, num_seqs=2, num_layers=1, num_q_heads=16, num_kv_heads=1, head_dim=128,
+              window=128, budget=30, seeds=3, radius=2, prior=("uniform", 10, 90), block_size=4),
 ]
 
 
