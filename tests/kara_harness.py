@@ -88,6 +88,21 @@ def unit_inputs(q_host: np.ndarray, k_pool_f64: np.ndarray, wl: Workload, n: int
     return qg, kw
 
 
+def oracle_unit_attention(q_heads: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray) -> np.ndarray:
+    """The oracle's paged decode attention for one KV head's query heads over
+    the unit's cached rows [0, T), given in logical order: the rows form a
+    one-sequence, one-layer pool of block size 1 with an identity table.
+    q_heads [G][d], k_rows / v_rows [T][d]; returns [G][d] in fp64."""
+    G, d = q_heads.shape
+    T = k_rows.shape[0]
+    pool_k = np.asarray(k_rows, dtype=np.float64).reshape(1, T, 1, 1, d)
+    pool_v = np.asarray(v_rows, dtype=np.float64).reshape(1, T, 1, 1, d)
+    table = np.arange(max(T, 1), dtype=np.int64).reshape(1, -1)
+    o = oracle.paged_decode_attention(np.asarray(q_heads, dtype=np.float64).reshape(1, 1, G, d), pool_k, pool_v,
+                                      table, np.array([T]), 1)
+    return o[0, 0]
+
+
 def score_errors(c_gpu: np.ndarray, c_orc: np.ndarray) -> np.ndarray:
     """|c_gpu - c_orc| / max(c_orc, floor), elementwise."""
     return np.abs(c_gpu.astype(np.float64) - c_orc) / np.maximum(c_orc, SCORE_FLOOR)

@@ -16,7 +16,7 @@ import oracle
 from decode_kv_cache_amd import kara as K
 from decode_kv_cache_amd.workloads import KaraShape, decode_queries, fill_prior_context, make_workload, \
     shape_by_name
-from tests.kara_harness import bits, config_of, run_step
+from tests.kara_harness import bits, config_of, oracle_unit_attention, run_step
 
 pytestmark = pytest.mark.gpu
 
@@ -120,6 +120,36 @@ def test_empty_short_and_split_lengths():
                                         s.block_size)
     assert np.all(got[0] == 0)
     _check(got, ref, "lengths")
+
+
+def test_block_table_cap_splits():
+    # 2048 units at block size 1 with about 10^4 slots each: one split per
+    # unit would stage more block ids than the kernel's LDS table holds, so
+    # the slot range is split because of that cap, not for occupancy.
+    # Sampled units are checked against the oracle.
+    s = KaraShape("attn_tblcap", 208, num_seqs=16, num_layers=16, num_q_heads=8, num_kv_heads=8, head_dim=64,
+                  window=64, budget=16, seeds=1, radius=1, prior=("fixed", 10000), block_size=1)
+    wl = make_workload(s, "cuda")
+    fill_prior_context(wl)
+    q_dec = decode_queries(s, "cuda")
+    cfg = config_of(wl)
+    assert s.units >= 2048 and K.kara_decode_attention_splits(cfg) >= 3
+    lens = (wl.host_prior_lens + s.window).astype(np.int32)
+    got = _attend(cfg, wl, q_dec, torch.from_numpy(lens).cuda())
+    assert np.all(np.isfinite(got))
+    rng = np.random.default_rng(208)
+    units = {(0, 0, 0), (s.num_seqs - 1, s.num_layers - 1, s.num_kv_heads - 1)}
+    while len(units) < 6:
+        units.add((int(rng.integers(s.num_seqs)), int(rng.integers(s.num_layers)), int(rng.integers(s.num_kv_heads))))
+    for (n, layer, g) in sorted(units):
+        T = int(lens[n])
+        blk = torch.from_numpy(wl.host_tables[n, :T].astype(np.int64)).cuda()
+        Kd = wl.k_pool[layer][blk, g, 0, :].float().double().cpu().numpy()
+        Vd = wl.v_pool[layer][blk, g, 0, :].float().double().cpu().numpy()
+        qh = q_dec[n, layer, g * s.group:(g + 1) * s.group].float().double().cpu().numpy()
+        _check(got[n, layer, g * s.group:(g + 1) * s.group], oracle_unit_attention(qh, Kd, Vd), (n, layer, g))
+    del wl
+    torch.cuda.empty_cache()
 
 
 def test_decode_attention_rejects_bad_arguments():

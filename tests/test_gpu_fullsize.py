@@ -7,7 +7,7 @@ import torch
 
 import oracle
 from decode_kv_cache_amd.workloads import make_workload, shape_by_name
-from tests.kara_harness import SCORE_RTOL, near_cutoff_ok, run_step, score_errors
+from tests.kara_harness import SCORE_RTOL, near_cutoff_ok, oracle_unit_attention, run_step, score_errors
 
 pytestmark = pytest.mark.gpu
 
@@ -177,11 +177,9 @@ def test_full_size_decode_attention_after_compaction():
         print(f"[attention] oracle on unit {(n, layer, g)}, {T} slots", flush=True)
         Kd = _unit_rows(wl, wl.k_pool, n, layer, g, 0, T).float().double().cpu().numpy()
         Vd = _unit_rows(wl, wl.v_pool, n, layer, g, 0, T).float().double().cpu().numpy()
-        for h in range(g * G, (g + 1) * G):
-            q = q_dec[n, layer, h].float().double().cpu().numpy()
-            z = Kd @ q / np.sqrt(d)
-            p = np.exp(z - z.max())
-            o = (p / p.sum()) @ Vd
-            assert np.all(np.abs(att_h[n, layer, h] - o) <= ATTN_ATOL + ATTN_RTOL * np.abs(o)), (n, layer, h)
+        qh = q_dec[n, layer, g * G:(g + 1) * G].float().double().cpu().numpy()
+        o = oracle_unit_attention(qh, Kd, Vd)
+        got = att_h[n, layer, g * G:(g + 1) * G]
+        assert np.all(np.abs(got - o) <= ATTN_ATOL + ATTN_RTOL * np.abs(o)), (n, layer, g)
     del wl, out
     torch.cuda.empty_cache()
