@@ -1,9 +1,12 @@
 """Host-side tooling: bench refuses more than one GPU, kernel-name demangling
-and the rocprofv3 CSV summaries used for the traffic figures."""
+and the rocprofv3 CSV summaries used for the traffic figures; the binding
+fails loudly without its library and never passes host tensors on."""
 import json
 import os
 import subprocess
 import sys
+
+import pytest
 
 from decode_kv_cache_amd import profiling
 from tests.conftest import ROOT
@@ -55,3 +58,28 @@ def test_traffic_scales_by_the_copy_calibration(tmp_path, monkeypatch):
     k = rec["kernels"]["fused_score_kernel"]
     assert k["fetch_bytes"] == 500 * 1024 / 0.5 and k["write_bytes"] == 20 * 1024
     assert rec["score_bytes_per_launch"] == k["bytes"]
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    """No fallback: with libkara.so absent every entry point raises."""
+    from decode_kv_cache_amd import kara as K
+    monkeypatch.setattr(K, "_LIB_PATH", str(tmp_path / "libkara.so"))
+    monkeypatch.setattr(K, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        K.lib()
+    with pytest.raises(RuntimeError, match="missing"):
+        K.kara_check_config(K.kara_config())
+
+
+def test_binding_rejects_host_tensors():
+    """Device pointers only: a CPU tensor never reaches the library."""
+    import torch
+
+    from decode_kv_cache_amd import kara as K
+    from decode_kv_cache_amd.workloads import shape_by_name
+    s = shape_by_name("tiny")
+    cfg = K.make_config(s, max_blocks_per_seq=32, num_blocks=64)
+    scores = torch.zeros((s.num_seqs, s.num_layers, s.num_kv_heads, s.window), dtype=torch.float32)
+    kept = torch.zeros((s.num_seqs, s.num_layers, s.num_kv_heads, s.budget), dtype=torch.int32)
+    with pytest.raises(ValueError, match="device"):
+        K.kara_select_chunks(cfg, scores, kept)
