@@ -111,7 +111,11 @@ __global__ __launch_bounds__(256) void probe_rewrite(u32x4* buf, size_t n) {
 // MFMA / VALU co-issue: per iteration 4 independent 16x16x32 bf16 MFMAs
 // (MODE 0), 16 independent fp32 FMAs (MODE 1), both interleaved as MFMA, 4
 // FMAs, MFMA, ... (MODE 2), the MFMAs interleaved with 16 v_exp_f32 (MODE 3),
-// or the 16 v_exp_f32 alone (MODE 4).
+// or the 16 v_exp_f32 alone (MODE 4); modes 3 and 4 scale each exponent
+// argument with a multiply first.  MODE 5: 16 bare v_exp_f32 (the argument is
+// negated through the input modifier, no multiply); MODE 6: the 16 bare
+// v_exp_f32 interleaved with 16 independent fp32 FMAs on other registers,
+// which shows whether the exponential and the FMA pipelines overlap.
 template <int MODE>
 __global__ __launch_bounds__(512) void probe_coissue(float* out, int iters, float a) {
   bf16x8 x, y;
@@ -121,22 +125,76 @@ __global__ __launch_bounds__(512) void probe_coissue(float* out, int iters, floa
   }
   typedef float f32x4 __attribute__((ext_vector_type(4)));
   f32x4 c[4] = {};
-  float v[16];
-  for (int e = 0; e < 16; ++e) v[e] = threadIdx.x * 1e-3f + e;
+  float v[16], w[16];
+  for (int e = 0; e < 16; ++e) {
+    v[e] = threadIdx.x * 1e-3f + e * 1e-2f;
+    w[e] = threadIdx.x * 1e-3f - e;
+  }
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       if (MODE == 0 || MODE == 2 || MODE == 3) c[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, c[m], 0, 0, 0);
       if (MODE != 0) {
 #pragma unroll
-        for (int e = 4 * m; e < 4 * m + 4; ++e)
-          v[e] = MODE >= 3 ? __builtin_amdgcn_exp2f(v[e] * a) : __builtin_fmaf(v[e], a, 0.5f);
+        for (int e = 4 * m; e < 4 * m + 4; ++e) {
+          if (MODE >= 5) {
+            v[e] = __builtin_amdgcn_exp2f(-v[e]);
+            if (MODE == 6) w[e] = __builtin_fmaf(w[e], a, 0.5f);
+          } else {
+            v[e] = MODE >= 3 ? __builtin_amdgcn_exp2f(v[e] * a) : __builtin_fmaf(v[e], a, 0.5f);
+          }
+        }
+      }
+    }
+    if (MODE == 6) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);   // one transcendental
+        __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);   // then one other VALU instruction
       }
     }
   }
   float s = 0.f;
   for (int m = 0; m < 4; ++m) s += c[m][0] + c[m][1] + c[m][2] + c[m][3];
-  for (int e = 0; e < 16; ++e) s += v[e];
+  for (int e = 0; e < 16; ++e) s += v[e] + (MODE == 6 ? w[e] : 0.f);
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// MFMA / VALU co-issue with a fixed number of waves per SIMD: 96 KiB of LDS
+// keep one workgroup per compute unit, so `threads` / 256 waves share each
+// SIMD.  Per iteration: NM independent 16x16x32 bf16 MFMAs and NV independent
+// fp32 FMAs (VK = 0) or bare v_exp_f32 (VK = 1); with PAT the instruction
+// stream is MFMA, NV / NM vector instructions, MFMA, ...
+template <int NM, int NV, int VK, int PAT>
+__global__ __launch_bounds__(512, 1) void probe_coissue_cu(float* out, int iters, float a) {
+  extern __shared__ float lds_keep[];
+  bf16x8 x[8], y;
+  for (int i = 0; i < 8; ++i) {
+    y[i] = (__bf16)(i * 1e-3f);
+    for (int m = 0; m < 8; ++m) x[m][i] = (__bf16)(threadIdx.x * 1e-3f + m);
+  }
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  f32x4 c[NM > 0 ? NM : 1];
+  for (int m = 0; m < (NM > 0 ? NM : 1); ++m) c[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float v[NV > 0 ? NV : 1];
+  for (int e = 0; e < (NV > 0 ? NV : 1); ++e) v[e] = threadIdx.x * 1e-3f + e * 1e-2f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m) c[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x[m & 7], y, c[m], 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < NV; ++e) v[e] = VK == 0 ? __builtin_fmaf(v[e], a, 0.5f) : __builtin_amdgcn_exp2f(-v[e]);
+    if (PAT && NM > 0 && NV > 0) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, NM > 0 ? NV / NM : 1, 0);
+      }
+    }
+  }
+  float s = 0.f;
+  for (int m = 0; m < NM; ++m) s += c[m][0] + c[m][1] + c[m][2] + c[m][3];
+  for (int e = 0; e < NV; ++e) s += v[e];
+  if (s == 12345.f) lds_keep[threadIdx.x] = s;   // the LDS allocation stays
   out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
@@ -190,6 +248,26 @@ int kara_probe_coissue(int mode, float* out, int blocks, int threads, int iters,
     case 2: hipLaunchKernelGGL(probe_coissue<2>, g, b, 0, st, out, iters, 0.999f); break;
     case 3: hipLaunchKernelGGL(probe_coissue<3>, g, b, 0, st, out, iters, 0.999f); break;
     case 4: hipLaunchKernelGGL(probe_coissue<4>, g, b, 0, st, out, iters, 0.999f); break;
+    case 5: hipLaunchKernelGGL(probe_coissue<5>, g, b, 0, st, out, iters, 0.999f); break;
+    case 6: hipLaunchKernelGGL(probe_coissue<6>, g, b, 0, st, out, iters, 0.999f); break;
+    default: return -1;
+  }
+  return status(hipGetLastError());
+}
+
+int kara_probe_coissue_cu(int mode, float* out, int blocks, int threads, int iters, void* stream) {
+  if (!out || blocks < 1 || iters < 1 || (threads != 256 && threads != 512)) return -1;
+  const dim3 g(blocks), b(threads);
+  const size_t lds = 96 * 1024;
+  const hipStream_t st = (hipStream_t)stream;
+  switch (mode) {
+    case 0: hipLaunchKernelGGL((probe_coissue_cu<16, 0, 0, 0>), g, b, lds, st, out, iters, 0.999f); break;
+    case 1: hipLaunchKernelGGL((probe_coissue_cu<0, 64, 0, 0>), g, b, lds, st, out, iters, 0.999f); break;
+    case 2: hipLaunchKernelGGL((probe_coissue_cu<16, 16, 0, 1>), g, b, lds, st, out, iters, 0.999f); break;
+    case 3: hipLaunchKernelGGL((probe_coissue_cu<16, 32, 0, 1>), g, b, lds, st, out, iters, 0.999f); break;
+    case 4: hipLaunchKernelGGL((probe_coissue_cu<16, 64, 0, 1>), g, b, lds, st, out, iters, 0.999f); break;
+    case 5: hipLaunchKernelGGL((probe_coissue_cu<0, 32, 1, 0>), g, b, lds, st, out, iters, 0.999f); break;
+    case 6: hipLaunchKernelGGL((probe_coissue_cu<16, 32, 1, 1>), g, b, lds, st, out, iters, 0.999f); break;
     default: return -1;
   }
   return status(hipGetLastError());

@@ -310,15 +310,50 @@ def cmd_coissue(a):
         waves_per_simd = blocks * threads / 64 / simds
         return ev[0].elapsed_time(ev[1]) * 1e6 / iters / waves_per_simd
 
-    print("| Waves per SIMD | 4 MFMA | 16 FMA | 4 MFMA + 16 FMA | overlap | 16 v_exp_f32 | 4 MFMA + 16 v_exp_f32 "
-          "| overlap |")
-    print("|---|---|---|---|---|---|---|---|")
+    print("| Waves per SIMD | 4 MFMA | 16 FMA | 4 MFMA + 16 FMA | overlap | 16 (mul + v_exp_f32) "
+          "| 4 MFMA + 16 (mul + v_exp_f32) | overlap | 16 bare v_exp_f32 | 16 v_exp_f32 + 16 FMA | overlap |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|")
     for label, blocks, threads in (("1", cus, 256), ("2", cus, 512), ("4", 4 * cus, 256)):
-        tm, tf, tb, tmx, tx = (ns(m, blocks, threads) for m in (0, 1, 2, 3, 4))
+        tm, tf, tb, tmx, tx, te, tef = (ns(m, blocks, threads) for m in (0, 1, 2, 3, 4, 5, 6))
         ov = (tm + tf - tb) / min(tm, tf)
         ox = (tm + tx - tmx) / min(tm, tx)
+        oe = (te + tf - tef) / min(te, tf)
         print(f"| {label} | {tm:.1f} ns | {tf:.1f} ns | {tb:.1f} ns | {100 * ov:.0f} % | {tx:.1f} ns | {tmx:.1f} ns "
-              f"| {100 * ox:.0f} % |", flush=True)
+              f"| {100 * ox:.0f} % | {te:.1f} ns | {tef:.1f} ns | {100 * oe:.0f} % |", flush=True)
+
+
+def cmd_coissue_cu(a):
+    """Time kara_probe_coissue_cu's modes at exactly one and two waves per
+    SIMD (one workgroup per compute unit) and print ns per wave-iteration."""
+    import ctypes
+
+    import torch
+    path = os.path.join(ROOT, "decode_kv_cache_amd", "libkara_probes.so")
+    lib = ctypes.CDLL(path)
+    lib.kara_probe_coissue_cu.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_void_p]
+    lib.kara_probe_coissue_cu.restype = ctypes.c_int
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    st = torch.cuda.Stream()
+    sp = ctypes.c_void_p(st.cuda_stream)
+    out = torch.empty(cus * 512, dtype=torch.float32, device="cuda")
+    o = ctypes.c_void_p(out.data_ptr())
+    names = ["16 MFMA", "64 FMA", "16 MFMA + 16 FMA (M v)", "16 MFMA + 32 FMA (M vv)", "16 MFMA + 64 FMA (M vvvv)",
+             "32 v_exp_f32", "16 MFMA + 32 v_exp_f32 (M ee)"]
+    print("| Per iteration | 1 wave per SIMD | 2 waves per SIMD |")
+    print("|---|---|---|")
+    for mode, name in enumerate(names):
+        row = []
+        for threads in (256, 512):
+            if lib.kara_probe_coissue_cu(mode, o, cus, threads, 10, sp) != 0:
+                raise RuntimeError("probe launch failed")
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(st)
+            lib.kara_probe_coissue_cu(mode, o, cus, threads, a.iters, sp)
+            ev[1].record(st)
+            torch.cuda.synchronize()
+            row.append(ev[0].elapsed_time(ev[1]) * 1e6 / a.iters / (threads // 256))
+        print(f"| {name} | {row[0]:.1f} ns | {row[1]:.1f} ns |", flush=True)
 
 
 def cmd_compact_patterns(a):
@@ -404,11 +439,13 @@ def main(argv=None):
     t.add_argument("--copy-mib", type=int, required=True)
     ci = sub.add_parser("coissue")
     ci.add_argument("--iters", type=int, default=20000)
+    cc = sub.add_parser("coissue_cu")
+    cc.add_argument("--iters", type=int, default=4000)
     cp = sub.add_parser("compact_patterns")
     cp.add_argument("--workload", default="llama8b_b64")
     cp.add_argument("--reps", type=int, default=5)
     a = p.parse_args(argv)
-    {"coissue": cmd_coissue, "compact_patterns": cmd_compact_patterns, "copy": cmd_copy, "peaks": cmd_peaks, "stats": cmd_stats, "traffic": cmd_traffic,
+    {"coissue": cmd_coissue, "coissue_cu": cmd_coissue_cu, "compact_patterns": cmd_compact_patterns, "copy": cmd_copy, "peaks": cmd_peaks, "stats": cmd_stats, "traffic": cmd_traffic,
      "counters": cmd_counters}[a.cmd](a)
 
 

@@ -28,10 +28,21 @@ int kara_probe_fma(float* out, int blocks, int iters, void* stream);
 /* blocks x threads lanes (threads a multiple of 64, at most 512), iters iterations of:
  * mode 0: 4 independent MFMA 16x16x32 bf16; mode 1: 16 independent fp32 FMA; mode 2: both,
  * interleaved (MFMA, 4 FMA, MFMA, ...); mode 3: the MFMAs interleaved with 16 v_exp_f32;
- * mode 4: the 16 v_exp_f32 alone.
+ * mode 4: the 16 v_exp_f32 alone (modes 3 and 4 multiply each argument first); mode 5: 16
+ * bare v_exp_f32 (argument negated by the input modifier); mode 6: the 16 bare v_exp_f32
+ * interleaved with 16 independent fp32 FMAs.
  * out: blocks * threads floats.  Comparing the modes' times shows how far the matrix cores
  * and the VALU overlap at a given number of waves per SIMD. */
 int kara_probe_coissue(int mode, float* out, int blocks, int threads, int iters, void* stream);
+
+/* Co-issue at a fixed number of waves per SIMD: blocks workgroups of `threads` (256 or 512)
+ * lanes, each holding 96 KiB of LDS so that one workgroup runs per compute unit (pass
+ * blocks = number of compute units for threads / 256 waves per SIMD).  Per iteration:
+ * mode 0: 16 independent 16x16x32 bf16 MFMAs; mode 1: 64 independent fp32 FMAs;
+ * modes 2, 3, 4: the 16 MFMAs with 16, 32 or 64 FMAs interleaved (MFMA, 1/2/4 FMAs, ...);
+ * mode 5: 32 bare v_exp_f32; mode 6: the 16 MFMAs with the 32 v_exp_f32 interleaved.
+ * out: blocks * threads floats. */
+int kara_probe_coissue_cu(int mode, float* out, int blocks, int threads, int iters, void* stream);
 
 /* Reads `bytes` (a multiple of 16) of src once.  out: grid * 256 floats. */
 int kara_probe_read(const void* src, size_t bytes, float* out, int grid, void* stream);
