@@ -5,6 +5,7 @@ leg may import this package; the product path never does.
 """
 from .kara_oracle import (  # noqa: F401
     Selection,
+    batch_unit_scores,
     chunk_bound,
     compact_paged_sequence,
     compact_window_rows,

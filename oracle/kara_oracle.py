@@ -64,6 +64,7 @@ __all__ = [
     "compact_window_rows",
     "compact_paged_sequence",
     "rewrite_block_table",
+    "batch_unit_scores",
     "compress_step",
 ]
 
@@ -322,6 +323,22 @@ def paged_decode_attention(q_dec, k_pool, v_pool, block_tables, seq_lens, block_
 # --------------------------------------------------------------------------
 # The whole step over a batch
 # --------------------------------------------------------------------------
+def batch_unit_scores(q, k_pool, block_tables, prior_lens, n, layer, g, block_size):
+    """Window scores of unit (sequence n, layer, KV head g) inside a batch.
+
+    The unit's queries are the window queries of query heads g*G .. g*G+G-1 of
+    sequence n and layer ``layer`` (reading R4: contiguous GQA groups), and its
+    keys are the K rows of logical slots [L, L+W) of that sequence, layer and
+    KV head, L = prior_lens[n], read through the sequence's block table
+    (readings R3, R7).  Returns window_scores of the two.
+    """
+    _, _, W, Hq, _ = q.shape
+    G = Hq // k_pool.shape[2]
+    qg = np.transpose(q[n, layer, :, g * G:(g + 1) * G, :], (1, 0, 2))
+    kw = gather_window_rows(k_pool, block_tables[n], layer, g, int(prior_lens[n]), W, block_size)
+    return window_scores(qg, kw)
+
+
 def compress_step(q, k_pool, v_pool, block_tables, prior_lens, *, window, budget,
                   seeds, radius, block_size, scores_override=None, gap=0):
     """Run a1-a10 for every sequence, layer and KV head.
@@ -353,9 +370,8 @@ def compress_step(q, k_pool, v_pool, block_tables, prior_lens, *, window, budget
         for layer in range(layers):
             for g in range(Hkv):
                 if scores_override is None:
-                    qg = np.transpose(q[n, layer, :, g * G:(g + 1) * G, :], (1, 0, 2))
-                    kw = gather_window_rows(k_pool, block_tables[n], layer, g, L, W, block_size)
-                    scores[n, layer, g] = window_scores(qg, kw)
+                    scores[n, layer, g] = batch_unit_scores(q, k_pool, block_tables, prior_lens, n, layer, g,
+                                                            block_size)
                 else:
                     scores[n, layer, g] = np.asarray(scores_override[n, layer, g], dtype=np.float64)
                 if gap == 0:
