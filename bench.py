@@ -89,13 +89,30 @@ def _pool_init():
         pass
 
 
+def cpu_workers():
+    """Worker processes of the oracle pool: one per CPU this process may run
+    on, at most 16 (the host's CPU share per GPU)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, shape, target_s):
     """Time the oracle (score + select + compact per unit) on a seeded sample."""
     import multiprocessing as mp
 
     import numpy as np
     import torch
-    procs = max(1, min(16, os.cpu_count() or 1))
+    procs = cpu_workers()
     rng = np.random.default_rng(1234)
     G, W, bs = shape.group, shape.window, shape.block_size
 
@@ -127,6 +144,7 @@ def cpu_baseline(wl, shape, target_s):
     est_total = wall * units / n
     tokens = shape.num_seqs * shape.window
     return {"value": tokens / est_total, "unit": "window tokens/s", "cores": procs, "kind": "oracle",
+            "cpu_model": cpu_model(), "cpus_visible": len(os.sched_getaffinity(0)),
             "sample": f"{n} of {units} units (seeded), fp64 numpy score+select+compact per unit, "
                       f"{procs} worker processes x 1 BLAS thread, {wall:.1f} s wall; extrapolated linearly "
                       f"to all units"}
@@ -212,6 +230,12 @@ def main():
     torch.cuda.synchronize()
     if not tables_match(False):
         sys.exit("bench: block tables differ from the workload after a restore")
+    # the library's own check of the addressing data before any step trusts it
+    bad = torch.full((1,), -1, dtype=torch.int32, device=dev)
+    K.kara_validate_tables(cfg, wl.block_tables, wl.prior_lens, bad, st)
+    torch.cuda.synchronize()
+    if int(bad.item()) != 0:
+        sys.exit(f"bench: kara_validate_tables reports {int(bad.item())} sequences with out-of-range entries")
     for _ in range(a.warmup):
         restore()
         step()

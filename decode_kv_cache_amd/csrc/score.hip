@@ -277,14 +277,17 @@ __global__ __launch_bounds__(256) void col_mass_kernel(Geo g, const T* __restric
   const int L = prior[n];
   const int32_t* trow = tables + (long long)n * g.max_blocks;
 
-  // the wave's two key tiles (B operands)
+  // the wave's two key tiles (B operands); keys past the window are zeros
+  // and their columns are never written
   const int key0 = kb * PER_BLOCK + wave * PER_WAVE;
+  const unsigned char* kbytes = reinterpret_cast<const unsigned char*>(kc);
+  const PagedRows pr = paged_rows(g, trow, layer, kvh, L, (int)sizeof(T));
   typename M::frag bk[2][NF];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int j = key0 + s * TILE + col;
-    const long long off = j < g.W ? slot_offset(g, trow, layer, kvh, L + j) : -1;
-    load_half_row<T, D>(kc + (off < 0 ? 0 : off) + half * (D / 2), off >= 0, bk[s]);
+    const T* kp = reinterpret_cast<const T*>(kbytes + paged_row(pr, L + min(j, g.W - 1))) + half * (D / 2);
+    load_half_row<T, D>(kp, j < g.W, bk[s]);
   }
 
   // staging of Q row tile rt: this thread's chunks.  The element offset of

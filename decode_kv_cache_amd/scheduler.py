@@ -195,6 +195,11 @@ def compress(cache: PagedCache, seqs: list, q_windows: torch.Tensor, stream=None
     nfreed = torch.empty(m, dtype=torch.int32, device=dev)
     if record is not None:
         pre = dict(k=cache.k.clone(), v=cache.v.clone(), tables=cache.tables[idx].copy(), prior=prior.copy())
+    # every window block must map to a physical block before the kernels use it
+    bad = torch.full((1,), -1, dtype=torch.int32, device=dev)
+    K.kara_validate_tables(cfg, tables, prior_t, bad, stream)
+    if int(bad.cpu().item()) != 0:
+        raise RuntimeError(f"scheduler: {int(bad.cpu().item())} due sequences have out-of-range block-table entries")
     K.kara_score_window(cfg, q_windows, cache.k, tables, prior_t, scores, ws, stream)
     K.kara_select_chunks(cfg, scores, kept, None, stream)
     K.kara_compact_paged(cfg, cache.k, cache.v, tables, prior_t, seq_lens, kept, freed, nfreed, stream)

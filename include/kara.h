@@ -28,9 +28,12 @@
  *    returns an error has enqueued nothing and written nothing.
  *  - Device-side contents (block ids, prior lengths, kept lists) are not
  *    checked by the three step calls.  Kernels never access memory outside the
- *    buffers the configuration describes: a slot whose table entry is out of
- *    range is skipped, so the outputs for that sequence are unspecified.
- *    kara_validate_tables reports such entries.
+ *    buffers the configuration describes: a read through an out-of-range
+ *    table entry (negative or >= num_blocks) returns the row of physical block
+ *    0 (it exists whenever there is a sequence), and compaction neither reads
+ *    nor writes a slot whose entry is out of range.  The outputs for such a
+ *    sequence are unspecified.  kara_validate_tables reports such sequences;
+ *    call it before trusting tables built elsewhere.
  *
  * Layouts (row-major, contiguous, element type = cfg.dtype unless stated):
  *   q            [num_seqs][num_layers][window][num_q_heads][head_dim]  window queries
