@@ -20,6 +20,10 @@ hipError_t launch_pipeline(const Geo& g, const void* q, void* kc, void* vc, int3
                            float* scores, int32_t* kept, uint8_t* mask, int32_t* seq_lens, int32_t* freed,
                            int32_t* num_freed, int max_freed, int32_t* done, hipStream_t st);
 int decode_attn_splits(const Geo& g);
+hipError_t launch_pipeline_noalloc(const Geo& g, const void* q, void* kc, void* vc, int32_t* tables,
+                                   const int32_t* prior, float* scores, int32_t* kept, uint8_t* mask,
+                                   int32_t* seq_lens, int32_t* freed, int32_t* num_freed, int max_freed,
+                                   hipStream_t st);
 hipError_t launch_decode_attn(const Geo& g, int dtype, const void* q, const void* kc, const void* vc,
                               const int32_t* tables, const int32_t* lens, float* out, float* ws, hipStream_t st);
 }  // namespace kara
@@ -163,6 +167,30 @@ int kara_compress_fused(const kara_config* cfg, const void* q, void* k_cache, vo
                                           (hipStream_t)stream));
 }
 
+int kara_compress_fused_noalloc(const kara_config* cfg, const void* q, void* k_cache, void* v_cache,
+                                int32_t* block_tables, const int32_t* prior_lens, float* scores, int32_t* kept,
+                                uint8_t* mask, int32_t* seq_lens, int32_t* freed_blocks, int32_t* num_freed,
+                                void* stream) {
+  int s = check(cfg);
+  if (s) return s;
+  const kara::Geo g = geo(cfg);
+  if (!kara::fused_score_supported(g, cfg->dtype)) return KARA_ENOTIMPL;
+  if (cfg->num_seqs == 0) return KARA_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !prior_lens || !scores || !kept || !seq_lens || !freed_blocks ||
+      !num_freed)
+    return KARA_ENULL;
+  if (cfg->num_seqs > KARA_NOALLOC_MAX_SEQS) return KARA_ESCRATCH;
+  if (stream) {   // the scratch address is per device: the stream must run on the current one
+    int cur = -1, sdev = -1;
+    if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess)
+      return KARA_EINVAL;
+    if (cur != sdev) return KARA_EINVAL;
+  }
+  return hip_status(kara::launch_pipeline_noalloc(g, q, k_cache, v_cache, block_tables, prior_lens, scores, kept,
+                                                  mask, seq_lens, freed_blocks, num_freed, kara_max_freed(cfg),
+                                                  (hipStream_t)stream));
+}
+
 size_t kara_decode_attention_workspace_bytes(const kara_config* cfg) {
   if (check(cfg) != KARA_OK) return 0;
   return kara::decode_attn_workspace_bytes(geo(cfg));
@@ -216,6 +244,7 @@ const char* kara_status_str(int status) {
     case KARA_EWORKSPACE: return "workspace missing, misaligned or too small";
     case KARA_EHIP: return "HIP runtime error while enqueueing";
     case KARA_ENOTIMPL: return "not supported by this build";
+    case KARA_ESCRATCH: return "more sequences than the fixed scratch of an allocation-free entry point holds";
     default: return "unknown status";
   }
 }

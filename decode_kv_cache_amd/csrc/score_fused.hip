@@ -21,6 +21,8 @@
 //     blocks of the unit; they are reduced over the 16 query lanes once, at
 //     the end.
 // Each logit is computed once and exponentiated once.
+#include <mutex>
+
 #include "compact_core.h"
 #include "kara_device.h"
 #include "select_core.h"
@@ -357,6 +359,62 @@ hipError_t launch_pipeline(const Geo& g, const void* q, void* kc, void* vc, int3
                      (unsigned char*)kc, (unsigned char*)vc, tables, prior, scores, kept, mask, seq_lens, freed,
                      num_freed, max_freed, done);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free form of the single-launch pipeline.  Its per-sequence
+// arrival counters live in `scratch`, a fixed array of this module on every
+// GPU, instead of a caller buffer.  Host code never passes the array's name to
+// a kernel: the device address is looked up once per device with
+// hipGetSymbolAddress (with that device current) and kept.  The counters are
+// cleared by a fill kernel on the caller's stream before every pipeline
+// launch, so a call never depends on what an earlier call left behind; calls
+// that overlap on one GPU share the array and race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) int32_t scratch[KARA_NOALLOC_MAX_SEQS];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch[kMaxDevices] = {};
+}  // namespace
+
+__global__ void zero_counters_kernel(int32_t* __restrict__ c, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) c[i] = 0;
+}
+
+// Device address of `scratch` on the current device (looked up on first use).
+hipError_t noalloc_scratch(int32_t** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch[dev] = static_cast<int32_t*>(p);
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_pipeline_noalloc(const Geo& g, const void* q, void* kc, void* vc, int32_t* tables,
+                                   const int32_t* prior, float* scores, int32_t* kept, uint8_t* mask,
+                                   int32_t* seq_lens, int32_t* freed, int32_t* num_freed, int max_freed,
+                                   hipStream_t st) {
+  if (g.S > KARA_NOALLOC_MAX_SEQS) return hipErrorInvalidValue;
+  int32_t* done = nullptr;
+  hipError_t e = noalloc_scratch(&done);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(zero_counters_kernel, dim3((g.S + 255) / 256), dim3(256), 0, st, done, g.S);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_pipeline(g, q, kc, vc, tables, prior, scores, kept, mask, seq_lens, freed, num_freed, max_freed,
+                         done, st);
 }
 
 bool fused_score_supported(const Geo& g, int dtype) {

@@ -18,6 +18,7 @@ __all__ = [
     "kara_max_freed", "kara_score_passes", "kara_score_window", "kara_select_chunks", "kara_chunk_bound",
     "kara_select_chunks_bridged", "kara_compact_paged", "kara_decode_attention", "kara_decode_attention_splits",
     "kara_decode_attention_workspace_bytes", "kara_compress_fused", "kara_compress_fused_supported",
+    "kara_compress_fused_noalloc",
     "kara_validate_tables", "kara_status_str", "kara_last_hip_error", "KARA_BF16", "KARA_F32",
     "EXPORTED_SYMBOLS",
 ]
@@ -30,7 +31,7 @@ EXPORTED_SYMBOLS = ("kara_check_config", "kara_workspace_bytes", "kara_max_freed
                     "kara_select_chunks", "kara_chunk_bound", "kara_select_chunks_bridged",
                     "kara_compact_paged", "kara_decode_attention_workspace_bytes", "kara_decode_attention_splits",
                     "kara_decode_attention", "kara_compress_fused_supported", "kara_compress_fused",
-                    "kara_validate_tables", "kara_status_str",
+                    "kara_compress_fused_noalloc", "kara_validate_tables", "kara_status_str",
                     "kara_last_hip_error")
 
 
@@ -79,6 +80,7 @@ def lib() -> ctypes.CDLL:
             "kara_decode_attention": (i32, [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "kara_compress_fused_supported": (i32, [P]),
             "kara_compress_fused": (i32, [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+            "kara_compress_fused_noalloc": (i32, [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
             "kara_status_str": (ctypes.c_char_p, [i32]),
             "kara_last_hip_error": (i32, []),
         }
@@ -255,6 +257,28 @@ def kara_compress_fused(cfg, q, k_cache, v_cache, block_tables, prior_lens, scor
                                      _ptr(prior_lens), _ptr(scores), _ptr(kept), _ptr(mask), _ptr(seq_lens),
                                      _ptr(freed_blocks), _ptr(num_freed), _ptr(done), _stream(stream)),
            "kara_compress_fused")
+
+
+def kara_compress_fused_noalloc(cfg, q, k_cache, v_cache, block_tables, prior_lens, scores, kept, seq_lens,
+                                freed_blocks, num_freed, mask=None, stream=None):
+    S, Lyr, W, Hq, Hkv, d, B = (cfg.num_seqs, cfg.num_layers, cfg.window, cfg.num_q_heads, cfg.num_kv_heads,
+                                cfg.head_dim, cfg.budget)
+    _need(q, "q", _elem(cfg), (S, Lyr, W, Hq, d))
+    _need(k_cache, "k_cache", _elem(cfg), _pool_shape(cfg))
+    _need(v_cache, "v_cache", _elem(cfg), _pool_shape(cfg))
+    _need(block_tables, "block_tables", torch.int32, (S, cfg.max_blocks_per_seq))
+    _need(prior_lens, "prior_lens", torch.int32, (S,))
+    _need(scores, "scores", torch.float32, (S, Lyr, Hkv, W))
+    _need(kept, "kept", torch.int32, (S, Lyr, Hkv, B))
+    if mask is not None:
+        _need(mask, "mask", torch.uint8, (S, Lyr, Hkv, W))
+    _need(seq_lens, "seq_lens", torch.int32, (S,))
+    _need(freed_blocks, "freed_blocks", torch.int32, (S, kara_max_freed(cfg)))
+    _need(num_freed, "num_freed", torch.int32, (S,))
+    _check(lib().kara_compress_fused_noalloc(ctypes.byref(cfg), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                             _ptr(block_tables), _ptr(prior_lens), _ptr(scores), _ptr(kept),
+                                             _ptr(mask), _ptr(seq_lens), _ptr(freed_blocks), _ptr(num_freed),
+                                             _stream(stream)), "kara_compress_fused_noalloc")
 
 
 def kara_validate_tables(cfg, block_tables, prior_lens, bad_seqs, stream=None):

@@ -67,6 +67,10 @@ extern "C" {
 #define KARA_EWORKSPACE (-3) /* workspace missing or smaller than kara_workspace_bytes */
 #define KARA_EHIP (-4)       /* the HIP runtime reported an error while enqueueing */
 #define KARA_ENOTIMPL (-5)   /* valid request this build does not support */
+#define KARA_ESCRATCH (-6)   /* request larger than the fixed scratch of an allocation-free entry point */
+
+/* most sequences one kara_compress_fused_noalloc call may cover */
+#define KARA_NOALLOC_MAX_SEQS 65536
 
 /* element types of q, k_cache and v_cache */
 #define KARA_BF16 0
@@ -184,6 +188,26 @@ int kara_compress_fused(const kara_config* cfg, const void* q, void* k_cache, vo
                         int32_t* block_tables, const int32_t* prior_lens, float* scores, int32_t* kept,
                         uint8_t* mask, int32_t* seq_lens, int32_t* freed_blocks, int32_t* num_freed,
                         int32_t* done, void* stream);
+
+/*
+ * kara_compress_fused without caller scratch, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, layouts, results and
+ * errors as kara_compress_fused, except that the per-sequence counters live in
+ * a fixed array of KARA_NOALLOC_MAX_SEQS int32 that the library holds on every
+ * GPU it runs on (256 KiB each, until the process ends).  The call allocates
+ * nothing: on its first use on a device (which must be the current device,
+ * and the device of `stream`) it looks the array's address up once.  Every
+ * call clears the counters it uses on `stream` before the pipeline runs.
+ * Calls that overlap on one GPU share the array and race: serialise them
+ * (one stream, or events).  num_seqs > KARA_NOALLOC_MAX_SEQS gives
+ * KARA_ESCRATCH and enqueues nothing; a stream of another device gives
+ * KARA_EINVAL.
+ */
+int kara_compress_fused_noalloc(const kara_config* cfg, const void* q, void* k_cache, void* v_cache,
+                                int32_t* block_tables, const int32_t* prior_lens, float* scores, int32_t* kept,
+                                uint8_t* mask, int32_t* seq_lens, int32_t* freed_blocks, int32_t* num_freed,
+                                void* stream);
 
 /*
  * Consumer of the compacted cache: one decode step of paged attention (Kara

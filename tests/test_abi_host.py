@@ -137,3 +137,19 @@ def test_bridged_select_rejects_bad_gap_before_device_work():
     assert L.kara_select_chunks_bridged(ctypes.byref(c), 65, None, None, None, None) == -1
     assert L.kara_select_chunks_bridged(ctypes.byref(c), 8, None, None, None, None) == -1    # 9 + 12 > 20
     assert L.kara_select_chunks_bridged(ctypes.byref(c), 7, None, None, None, None) == -2    # 9 + 10 <= 20
+
+
+def test_allocation_free_pipeline_checks_before_device_work():
+    """kara_compress_fused_noalloc: configuration, support, NULL pointers and
+    the fixed scratch limit are all decided on the host, before any HIP call."""
+    L = K.lib()
+    n = None
+    p = ctypes.c_void_p(0x1000)
+    args = [p] * 11 + [n]                                                 # every pointer set, default stream
+    assert L.kara_compress_fused_noalloc(ctypes.byref(_cfg(budget=5000)), *args) == -1
+    assert L.kara_compress_fused_noalloc(ctypes.byref(_cfg(window=2048)), *args) == -5     # two-pass shape
+    assert L.kara_compress_fused_noalloc(ctypes.byref(_cfg()), *([n] * 11 + [n])) == -2
+    # one sequence past the fixed scratch; p is never dereferenced
+    assert L.kara_compress_fused_noalloc(ctypes.byref(_cfg(num_seqs=65537, num_layers=1)), *args) == -6
+    assert L.kara_compress_fused_noalloc(ctypes.byref(_cfg(num_seqs=0)), *args) == 0
+    assert "scratch" in K.kara_status_str(-6)

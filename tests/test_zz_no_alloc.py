@@ -1,0 +1,57 @@
+"""The allocation-free one-launch pipeline (kara_compress_fused_noalloc, for
+callers that cannot allocate device memory) against kara_compress_fused on the
+same seeded inputs, through the C ABI: calls in a row whose second one covers
+a smaller batch, every output, pool byte and table bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+from decode_kv_cache_amd import kara as K
+from decode_kv_cache_amd.workloads import KaraShape, make_workload
+from tests.kara_harness import Outputs, bits, config_of
+
+pytestmark = pytest.mark.gpu
+
+BIG = KaraShape("noalloc_big", 961, num_seqs=5, num_layers=2, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                window=300, budget=60, seeds=3, radius=4, prior=("uniform", 5, 80))
+SMALL = KaraShape("noalloc_small", 962, num_seqs=2, num_layers=1, num_q_heads=4, num_kv_heads=1, head_dim=128,
+                  window=160, budget=40, seeds=2, radius=3, prior=("uniform", 3, 40), block_size=8)
+
+
+def _run(shape, noalloc, stream=None):
+    wl = make_workload(shape, "cuda")
+    cfg = config_of(wl)
+    out = Outputs(cfg, "cuda")
+    torch.cuda.synchronize()
+    args = (cfg, wl.q, wl.k_pool, wl.v_pool, wl.block_tables, wl.prior_lens, out["scores"], out["kept"],
+            out["seq_lens"], out["freed"], out["num_freed"])
+    if noalloc:
+        K.kara_compress_fused_noalloc(*args, mask=out["mask"], stream=stream)
+    else:
+        done = torch.zeros(shape.num_seqs, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        K.kara_compress_fused(*args, done, mask=out["mask"], stream=stream)
+    torch.cuda.synchronize()
+    assert out.guards_intact()
+    res = {k: bits(out[k]) for k in ("scores", "kept", "mask", "seq_lens", "freed", "num_freed")}
+    res.update(k=bits(wl.k_pool), v=bits(wl.v_pool), tables=wl.block_tables.cpu().numpy())
+    return res
+
+
+def _same(a, b, what):
+    for k in a:
+        assert np.array_equal(a[k], b[k]), (what, k)
+
+
+def test_noalloc_matches_fused_on_calls_in_a_row():
+    print("[noalloc] big, then smaller, then big again", flush=True)
+    ref_big, ref_small = _run(BIG, False), _run(SMALL, False)
+    _same(ref_big, _run(BIG, True), "first call")
+    _same(ref_small, _run(SMALL, True), "second call, smaller batch")
+    _same(ref_big, _run(BIG, True), "third call")
+
+
+def test_noalloc_on_a_side_stream():
+    print("[noalloc] side stream", flush=True)
+    st = torch.cuda.Stream()
+    _same(_run(SMALL, False), _run(SMALL, True, stream=st), "side stream")
