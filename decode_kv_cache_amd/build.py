@@ -30,6 +30,8 @@ HIPCC_FLAGS = [
     "-fno-honor-nans",
     "-Wno-unused-result",
 ]
+# roctx ranges around the entry points (host-side trace markers)
+HIPCC_LIBS = ["-L/opt/rocm/lib", "-lrocprofiler-sdk-roctx", "-Wl,-rpath,/opt/rocm/lib"]
 
 
 def hipcc() -> str:
@@ -49,8 +51,9 @@ def build(verbose: bool = True, out: str = LIB, csrc: str = CSRC, extra=(), sour
 
 def _compile(verbose, out, csrc, extra, sources) -> str:
     tmp = out + ".tmp"
+    libs = HIPCC_LIBS if "api.hip" in sources else []
     cmd = [hipcc(), *HIPCC_FLAGS, *extra, f"-I{INCLUDE}", f"-I{csrc}",
-           *[os.path.join(csrc, s) for s in sources], "-o", tmp]
+           *[os.path.join(csrc, s) for s in sources], *libs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

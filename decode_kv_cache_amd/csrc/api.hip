@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/kara.h: argument checks,
 // geometry, and the launches of the gfx950 kernels.
 #include <math.h>
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include "kara_device.h"
 
@@ -40,6 +41,8 @@ int check(const kara_config* c) {
   if (c->num_q_heads % c->num_kv_heads) return KARA_EINVAL;
   if (c->head_dim != 64 && c->head_dim != 128) return KARA_EINVAL;
   if (c->window < 1 || c->window > 8192) return KARA_EINVAL;
+  // query rows per unit (G * W) are counted in int32 by the kernels
+  if ((long long)(c->num_q_heads / c->num_kv_heads) * c->window > (1LL << 24)) return KARA_EINVAL;
   if (c->budget < 1 || c->budget > c->window) return KARA_EINVAL;
   if (c->seeds < 0 || c->radius < 0 || c->radius > c->window) return KARA_EINVAL;
   if ((long long)c->seeds * (2LL * c->radius + 1) > c->budget) return KARA_EINVAL;
@@ -78,6 +81,15 @@ kara::Geo geo(const kara_config* c) {
   return g;
 }
 
+// A roctx range around one entry point's enqueue work, named after the entry
+// point, so host-side traces (rocprofv3 --marker-trace) show each call.
+struct Range {
+  explicit Range(const char* name) { roctxRangePushA(name); }
+  ~Range() { roctxRangePop(); }
+  Range(const Range&) = delete;
+  Range& operator=(const Range&) = delete;
+};
+
 int hip_status(hipError_t e) {
   if (e == hipSuccess) return KARA_OK;
   g_last_hip = (int)e;
@@ -111,6 +123,7 @@ int32_t kara_max_freed(const kara_config* cfg) {
 int kara_score_window(const kara_config* cfg, const void* q, const void* k_cache, const int32_t* block_tables,
                       const int32_t* prior_lens, float* scores, void* workspace, size_t workspace_bytes,
                       void* stream) {
+  const Range range("kara_score_window");
   int s = check(cfg);
   if (s) return s;
   if (cfg->num_seqs == 0) return KARA_OK;
@@ -123,6 +136,7 @@ int kara_score_window(const kara_config* cfg, const void* q, const void* k_cache
 }
 
 int kara_select_chunks(const kara_config* cfg, const float* scores, int32_t* kept, uint8_t* mask, void* stream) {
+  const Range range("kara_select_chunks");
   int s = check(cfg);
   if (s) return s;
   if (cfg->num_seqs == 0) return KARA_OK;
@@ -138,6 +152,7 @@ int64_t kara_chunk_bound(const kara_config* cfg, int32_t gap) {
 
 int kara_select_chunks_bridged(const kara_config* cfg, int32_t gap, const float* scores, int32_t* kept,
                                uint8_t* mask, void* stream) {
+  const Range range("kara_select_chunks_bridged");
   int s = check(cfg);
   if (s) return s;
   if (gap < 0 || gap > cfg->window || kara_chunk_bound(cfg, gap) > cfg->budget) return KARA_EINVAL;
@@ -154,6 +169,7 @@ int kara_compress_fused_supported(const kara_config* cfg) {
 int kara_compress_fused(const kara_config* cfg, const void* q, void* k_cache, void* v_cache, int32_t* block_tables,
                         const int32_t* prior_lens, float* scores, int32_t* kept, uint8_t* mask, int32_t* seq_lens,
                         int32_t* freed_blocks, int32_t* num_freed, int32_t* done, void* stream) {
+  const Range range("kara_compress_fused");
   int s = check(cfg);
   if (s) return s;
   const kara::Geo g = geo(cfg);
@@ -171,6 +187,7 @@ int kara_compress_fused_noalloc(const kara_config* cfg, const void* q, void* k_c
                                 int32_t* block_tables, const int32_t* prior_lens, float* scores, int32_t* kept,
                                 uint8_t* mask, int32_t* seq_lens, int32_t* freed_blocks, int32_t* num_freed,
                                 void* stream) {
+  const Range range("kara_compress_fused_noalloc");
   int s = check(cfg);
   if (s) return s;
   const kara::Geo g = geo(cfg);
@@ -204,6 +221,7 @@ int kara_decode_attention_splits(const kara_config* cfg) {
 int kara_decode_attention(const kara_config* cfg, const void* q_dec, const void* k_cache, const void* v_cache,
                           const int32_t* block_tables, const int32_t* seq_lens, float* out, void* workspace,
                           size_t workspace_bytes, void* stream) {
+  const Range range("kara_decode_attention");
   int s = check(cfg);
   if (s) return s;
   if (cfg->num_seqs == 0) return KARA_OK;
@@ -218,6 +236,7 @@ int kara_decode_attention(const kara_config* cfg, const void* q_dec, const void*
 int kara_compact_paged(const kara_config* cfg, void* k_cache, void* v_cache, int32_t* block_tables,
                        const int32_t* prior_lens, int32_t* seq_lens, const int32_t* kept, int32_t* freed_blocks,
                        int32_t* num_freed, void* stream) {
+  const Range range("kara_compact_paged");
   int s = check(cfg);
   if (s) return s;
   if (cfg->num_seqs == 0) return KARA_OK;
@@ -230,6 +249,7 @@ int kara_compact_paged(const kara_config* cfg, void* k_cache, void* v_cache, int
 
 int kara_validate_tables(const kara_config* cfg, const int32_t* block_tables, const int32_t* prior_lens,
                          int32_t* bad_seqs, void* stream) {
+  const Range range("kara_validate_tables");
   int s = check(cfg);
   if (s) return s;
   if (!bad_seqs || (cfg->num_seqs > 0 && (!block_tables || !prior_lens))) return KARA_ENULL;

@@ -79,7 +79,7 @@ extern "C" {
 typedef struct kara_config {
   int32_t num_seqs;      /* >= 0 (0 = nothing to do) */
   int32_t num_layers;    /* >= 1 */
-  int32_t num_q_heads;   /* >= 1, multiple of num_kv_heads */
+  int32_t num_q_heads;   /* >= 1, multiple of num_kv_heads, (num_q_heads / num_kv_heads) * window <= 2^24 */
   int32_t num_kv_heads;  /* >= 1 */
   int32_t head_dim;      /* 64 or 128 */
   int32_t window;        /* W, 1..8192 */

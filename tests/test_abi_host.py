@@ -66,6 +66,13 @@ def test_logical_positions_fit_int32():
     assert K.kara_check_config(_cfg(max_blocks_per_seq=2 ** 30 // 16 + 1)) == -1
 
 
+def test_query_rows_per_unit_are_bounded():
+    # G * W <= 2^24: the kernels count a unit's query rows in int32
+    assert K.kara_check_config(_cfg(num_q_heads=2048 * 8, window=8192, budget=100)) == 0      # G = 2048
+    assert K.kara_check_config(_cfg(num_q_heads=2049 * 8, window=8192, budget=100)) == -1
+    assert K.kara_check_config(_cfg(num_q_heads=2 ** 30, num_kv_heads=8)) == -1
+
+
 def test_seed_span_constraint_is_exact():
     assert K.kara_check_config(_cfg(seeds=17, radius=5, budget=187)) == 0      # 17 * 11 = 187
     assert K.kara_check_config(_cfg(seeds=17, radius=5, budget=186)) == -1
