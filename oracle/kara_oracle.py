@@ -45,6 +45,10 @@ Readings taken where the pages are silent (each is stated where used):
 * R14-R18 compaction is in place: logical slot L + r receives the row that
   sat in slot L + kept[r]; block-table entries past the new length are freed
   in ascending logical order and set to -1; every other byte is unchanged.
+* R28     when the window is the oldest part of the context not yet
+  compressed (the lay explainers, part 3, describe cleaning the back end of
+  the current thought), the newer tokens behind it move down, in order,
+  right after the kept rows.
 
 Parity pins for each function live in ``tests/test_oracle_*.py``.
 """
@@ -241,22 +245,32 @@ def compact_window_rows(rows, kept):
     return out
 
 
-def compact_paged_sequence(k_pool, v_pool, table_row, prior_len, kept, block_size):
+def compact_paged_sequence(k_pool, v_pool, table_row, prior_len, kept, block_size, *, window=None, tail=0):
     """Apply the compaction of every (layer, kv head) of one sequence, in place.
 
     ``kept`` is [layers][kv_heads][B].  For each (layer, head) and r < B, the
     K and V rows of logical slot prior_len + r become the old rows of slot
     prior_len + kept[r]; all old rows are read before any is written.
+
+    ``tail`` > 0 (reading R28: the window is the oldest part of the context
+    not yet compressed, and ``tail`` newer tokens follow it in the slots
+    [prior_len + window, prior_len + window + tail)) moves those tokens, in
+    order, right behind the kept rows: slot prior_len + B + t takes the old
+    row of slot prior_len + window + t.  ``window`` is then required.
     """
     layers, kv_heads, B = kept.shape
+    if tail < 0 or (tail > 0 and window is None):
+        raise ValueError("a tail needs the window length, and cannot be negative")
     for pool in (k_pool, v_pool):
         for layer in range(layers):
             for g in range(kv_heads):
+                src = [prior_len + int(j) for j in kept[layer, g]]
+                src += [prior_len + window + t for t in range(tail)]
                 old = []
-                for j in kept[layer, g]:
-                    blk, off = _slot(table_row, prior_len + int(j), block_size)
+                for p in src:
+                    blk, off = _slot(table_row, p, block_size)
                     old.append(pool[layer, blk, g, off].copy())
-                for r in range(B):
+                for r in range(len(src)):
                     blk, off = _slot(table_row, prior_len + r, block_size)
                     pool[layer, blk, g, off] = old[r]
 
@@ -264,19 +278,21 @@ def compact_paged_sequence(k_pool, v_pool, table_row, prior_len, kept, block_siz
 # --------------------------------------------------------------------------
 # a10: block-table rewrite and freed list  (R16, R17)
 # --------------------------------------------------------------------------
-def rewrite_block_table(table_row, prior_len, window, budget, block_size):
+def rewrite_block_table(table_row, prior_len, window, budget, block_size, tail=0):
     """Truncate one sequence's block table after compaction.
 
-    Blocks holding logical slots < prior_len + budget stay; the entries of
-    logical blocks ceil((L+B)/bs) .. ceil((L+W)/bs)-1 are returned in that
-    order as freed and replaced by -1.  Returns (new_row, freed, new_len).
+    Blocks holding logical slots < prior_len + budget + tail stay; the
+    entries of logical blocks ceil((L+B+T)/bs) .. ceil((L+W+T)/bs)-1 are
+    returned in that order as freed and replaced by -1 (T = tail, the newer
+    tokens that followed the window and moved down behind the kept rows; 0
+    when the window ends the sequence).  Returns (new_row, freed, new_len).
     """
     row = np.array(table_row, copy=True)
-    nb_old = -(-(prior_len + window) // block_size)
-    nb_new = -(-(prior_len + budget) // block_size)
+    nb_old = -(-(prior_len + window + tail) // block_size)
+    nb_new = -(-(prior_len + budget + tail) // block_size)
     freed = row[nb_new:nb_old].copy()
     row[nb_new:nb_old] = -1
-    return row, freed, prior_len + budget
+    return row, freed, prior_len + budget + tail
 
 
 # --------------------------------------------------------------------------
@@ -340,7 +356,7 @@ def batch_unit_scores(q, k_pool, block_tables, prior_lens, n, layer, g, block_si
 
 
 def compress_step(q, k_pool, v_pool, block_tables, prior_lens, *, window, budget,
-                  seeds, radius, block_size, scores_override=None, gap=0):
+                  seeds, radius, block_size, scores_override=None, gap=0, tail_lens=None):
     """Run a1-a10 for every sequence, layer and KV head.
 
     q            [S][layers][W][Hq][d]
@@ -351,6 +367,8 @@ def compress_step(q, k_pool, v_pool, block_tables, prior_lens, *, window, budget
                  instead of the oracle's own (used to pin the selection and
                  compaction stages to scores computed elsewhere).
     gap          0: the main Token2Chunk rule; > 0: the bridging variant.
+    tail_lens    optional [S]: newer tokens that follow each window and move
+                 down behind its kept rows (see compact_paged_sequence).
     Returns a dict with scores, kept, k_pool, v_pool, block_tables, seq_lens,
     freed (list of arrays) and num_freed.
     """
@@ -379,8 +397,9 @@ def compress_step(q, k_pool, v_pool, block_tables, prior_lens, *, window, budget
                 else:
                     sel = token2chunk_bridge_select(scores[n, layer, g], budget, seeds, radius, gap)
                 kept[n, layer, g] = sel.kept
-        compact_paged_sequence(k_out, v_out, block_tables[n], L, kept[n], block_size)
-        row, fr, new_len = rewrite_block_table(block_tables[n], L, W, budget, block_size)
+        T = 0 if tail_lens is None else int(tail_lens[n])
+        compact_paged_sequence(k_out, v_out, block_tables[n], L, kept[n], block_size, window=W, tail=T)
+        row, fr, new_len = rewrite_block_table(block_tables[n], L, W, budget, block_size, tail=T)
         tables[n] = row
         freed.append(fr)
         num_freed[n] = fr.size
