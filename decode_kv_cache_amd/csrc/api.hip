@@ -13,7 +13,7 @@ bool fused_score_supported(const Geo& g, int dtype);
 hipError_t launch_select(const Geo& g, int gap, const float* scores, int32_t* kept, uint8_t* mask, hipStream_t st);
 hipError_t launch_compact(const Geo& g, int dtype, void* kc, void* vc, int32_t* tables, const int32_t* prior,
                           int32_t* seq_lens, const int32_t* kept, int32_t* freed, int32_t* num_freed,
-                          int max_freed, hipStream_t st);
+                          int max_freed, const int32_t* tails, hipStream_t st);
 hipError_t launch_validate(const Geo& g, const int32_t* tables, const int32_t* prior, int32_t* bad,
                            hipStream_t st);
 size_t decode_attn_workspace_bytes(const Geo& g);
@@ -243,7 +243,22 @@ int kara_compact_paged(const kara_config* cfg, void* k_cache, void* v_cache, int
   if (!k_cache || !v_cache || !block_tables || !prior_lens || !seq_lens || !kept || !freed_blocks || !num_freed)
     return KARA_ENULL;
   return hip_status(kara::launch_compact(geo(cfg), cfg->dtype, k_cache, v_cache, block_tables, prior_lens,
-                                         seq_lens, kept, freed_blocks, num_freed, kara_max_freed(cfg),
+                                         seq_lens, kept, freed_blocks, num_freed, kara_max_freed(cfg), nullptr,
+                                         (hipStream_t)stream));
+}
+
+int kara_compact_paged_tail(const kara_config* cfg, void* k_cache, void* v_cache, int32_t* block_tables,
+                            const int32_t* prior_lens, const int32_t* tail_lens, int32_t* seq_lens,
+                            const int32_t* kept, int32_t* freed_blocks, int32_t* num_freed, void* stream) {
+  const Range range("kara_compact_paged_tail");
+  int s = check(cfg);
+  if (s) return s;
+  if (cfg->num_seqs == 0) return KARA_OK;
+  if (!k_cache || !v_cache || !block_tables || !prior_lens || !tail_lens || !seq_lens || !kept || !freed_blocks ||
+      !num_freed)
+    return KARA_ENULL;
+  return hip_status(kara::launch_compact(geo(cfg), cfg->dtype, k_cache, v_cache, block_tables, prior_lens,
+                                         seq_lens, kept, freed_blocks, num_freed, kara_max_freed(cfg), tail_lens,
                                          (hipStream_t)stream));
 }
 

@@ -17,27 +17,30 @@ __global__ __launch_bounds__(CMP_THREADS) void compact_kernel(Geo g, unsigned ch
                                                               unsigned char* __restrict__ vc,
                                                               const int32_t* __restrict__ tables,
                                                               const int32_t* __restrict__ prior,
-                                                              const int32_t* __restrict__ kept, int esize) {
+                                                              const int32_t* __restrict__ kept,
+                                                              const int32_t* __restrict__ tails, int esize) {
   const long long unit = blockIdx.x;
   const int kvh = (int)(unit % g.Hkv);
   const int layer = (int)((unit / g.Hkv) % g.Lyr);
   const int n = (int)(unit / ((long long)g.Hkv * g.Lyr));
+  const int L = prior[n];
   compact_unit_rows<CMP_THREADS, ROWBYTES, CMP_VEC>(g, kc, vc, tables + (long long)n * g.max_blocks, layer, kvh,
-                                                   prior[n], kept + unit * g.B, esize);
+                                                   L, kept + unit * g.B, esize, tail_of(g, tails, n, L));
 }
 
 // One thread per sequence: freed list, table truncation, new length.
 __global__ void finalize_kernel(Geo g, int32_t* __restrict__ tables, const int32_t* __restrict__ prior,
                                 int32_t* __restrict__ seq_lens, int32_t* __restrict__ freed,
-                                int32_t* __restrict__ num_freed, int max_freed) {
+                                int32_t* __restrict__ num_freed, int max_freed,
+                                const int32_t* __restrict__ tails) {
   const int n = blockIdx.x * blockDim.x + threadIdx.x;
   if (n >= g.S) return;
-  finalize_sequence(g, n, tables, prior, seq_lens, freed, num_freed, max_freed);
+  finalize_sequence(g, n, tables, prior, seq_lens, freed, num_freed, max_freed, tails);
 }
 
 hipError_t launch_compact(const Geo& g, int dtype, void* kc, void* vc, int32_t* tables, const int32_t* prior,
                           int32_t* seq_lens, const int32_t* kept, int32_t* freed, int32_t* num_freed,
-                          int max_freed, hipStream_t st) {
+                          int max_freed, const int32_t* tails, hipStream_t st) {
   const long long units = (long long)g.S * g.Lyr * g.Hkv;
   if (units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const int esize = dtype == KARA_BF16 ? 2 : 4;
@@ -46,16 +49,16 @@ hipError_t launch_compact(const Geo& g, int dtype, void* kc, void* vc, int32_t* 
     const dim3 grid((unsigned)units);
     if (rowbytes == 128)
       hipLaunchKernelGGL(compact_kernel<128>, grid, dim3(CMP_THREADS), 0, st, g, (unsigned char*)kc,
-                         (unsigned char*)vc, tables, prior, kept, esize);
+                         (unsigned char*)vc, tables, prior, kept, tails, esize);
     else if (rowbytes == 256)
       hipLaunchKernelGGL(compact_kernel<256>, grid, dim3(CMP_THREADS), 0, st, g, (unsigned char*)kc,
-                         (unsigned char*)vc, tables, prior, kept, esize);
+                         (unsigned char*)vc, tables, prior, kept, tails, esize);
     else
       hipLaunchKernelGGL(compact_kernel<512>, grid, dim3(CMP_THREADS), 0, st, g, (unsigned char*)kc,
-                         (unsigned char*)vc, tables, prior, kept, esize);
+                         (unsigned char*)vc, tables, prior, kept, tails, esize);
   }
   hipLaunchKernelGGL(finalize_kernel, dim3((g.S + 255) / 256), dim3(256), 0, st, g, tables, prior, seq_lens,
-                     freed, num_freed, max_freed);
+                     freed, num_freed, max_freed, tails);
   return hipGetLastError();
 }
 

@@ -16,7 +16,8 @@ import torch
 __all__ = [
     "KaraError", "kara_config", "make_config", "lib", "kara_check_config", "kara_workspace_bytes",
     "kara_max_freed", "kara_score_passes", "kara_score_window", "kara_select_chunks", "kara_chunk_bound",
-    "kara_select_chunks_bridged", "kara_compact_paged", "kara_decode_attention", "kara_decode_attention_splits",
+    "kara_select_chunks_bridged", "kara_compact_paged", "kara_compact_paged_tail", "kara_decode_attention",
+    "kara_decode_attention_splits",
     "kara_decode_attention_workspace_bytes", "kara_compress_fused", "kara_compress_fused_supported",
     "kara_compress_fused_noalloc",
     "kara_validate_tables", "kara_status_str", "kara_last_hip_error", "KARA_BF16", "KARA_F32",
@@ -29,7 +30,8 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkara.so
 EXPORTED_SYMBOLS = ("kara_check_config", "kara_workspace_bytes", "kara_max_freed", "kara_score_passes",
                     "kara_score_window",
                     "kara_select_chunks", "kara_chunk_bound", "kara_select_chunks_bridged",
-                    "kara_compact_paged", "kara_decode_attention_workspace_bytes", "kara_decode_attention_splits",
+                    "kara_compact_paged", "kara_compact_paged_tail", "kara_decode_attention_workspace_bytes",
+                    "kara_decode_attention_splits",
                     "kara_decode_attention", "kara_compress_fused_supported", "kara_compress_fused",
                     "kara_compress_fused_noalloc", "kara_validate_tables", "kara_status_str",
                     "kara_last_hip_error")
@@ -74,6 +76,7 @@ def lib() -> ctypes.CDLL:
             "kara_chunk_bound": (ctypes.c_int64, [P, ctypes.c_int32]),
             "kara_select_chunks_bridged": (i32, [P, ctypes.c_int32, vp, vp, vp, vp]),
             "kara_compact_paged": (i32, [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+            "kara_compact_paged_tail": (i32, [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
             "kara_validate_tables": (i32, [P, vp, vp, vp, vp]),
             "kara_decode_attention_workspace_bytes": (sz, [P]),
             "kara_decode_attention_splits": (i32, [P]),
@@ -208,6 +211,24 @@ def kara_compact_paged(cfg, k_cache, v_cache, block_tables, prior_lens, seq_lens
     _check(lib().kara_compact_paged(ctypes.byref(cfg), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                     _ptr(prior_lens), _ptr(seq_lens), _ptr(kept), _ptr(freed_blocks),
                                     _ptr(num_freed), _stream(stream)), "kara_compact_paged")
+
+
+def kara_compact_paged_tail(cfg, k_cache, v_cache, block_tables, prior_lens, tail_lens, seq_lens, kept,
+                            freed_blocks, num_freed, stream=None):
+    S = cfg.num_seqs
+    _need(k_cache, "k_cache", _elem(cfg), _pool_shape(cfg))
+    _need(v_cache, "v_cache", _elem(cfg), _pool_shape(cfg))
+    _need(block_tables, "block_tables", torch.int32, (S, cfg.max_blocks_per_seq))
+    _need(prior_lens, "prior_lens", torch.int32, (S,))
+    _need(tail_lens, "tail_lens", torch.int32, (S,))
+    _need(seq_lens, "seq_lens", torch.int32, (S,))
+    _need(kept, "kept", torch.int32, (S, cfg.num_layers, cfg.num_kv_heads, cfg.budget))
+    _need(freed_blocks, "freed_blocks", torch.int32, (S, kara_max_freed(cfg)))
+    _need(num_freed, "num_freed", torch.int32, (S,))
+    _check(lib().kara_compact_paged_tail(ctypes.byref(cfg), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                         _ptr(prior_lens), _ptr(tail_lens), _ptr(seq_lens), _ptr(kept),
+                                         _ptr(freed_blocks), _ptr(num_freed), _stream(stream)),
+           "kara_compact_paged_tail")
 
 
 def kara_decode_attention_workspace_bytes(cfg: kara_config) -> int:

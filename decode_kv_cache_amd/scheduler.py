@@ -10,17 +10,21 @@ sequences, so that compression never stalls the whole batch at once.
 Reading taken here (the pages give no algorithm):
 
 * every ``period`` decode steps the scheduler ticks; at a tick a sequence is
-  due when it has generated at least ``window`` tokens since its last
-  compression (its uncompressed tail); at most ``max_per_tick`` due
-  sequences are compressed, longest tail first, the rest wait for a later
-  tick (staggering);
-* a compressed sequence's window is its most recent ``window`` slots,
-  logical [len - window, len): everything before is prior context, which the
-  step never reads or writes (tokens of the tail that fall before the window
-  stay uncompressed);
+  due when its generated context that was never compressed (its tail, which
+  starts at ``base``: the prompt length, then the end of the last kept rows)
+  holds at least ``window`` tokens; at most ``max_per_tick`` due sequences
+  are compressed, longest tail first, the rest wait for a later tick
+  (staggering);
+* a compressed sequence's window is the oldest ``window`` tokens of that
+  tail, logical [base, base + window) (reading R28, the explainer's "back
+  end of the current thought"); everything before is prior context, which
+  the step never reads or writes, and the T = tail - window newer tokens
+  behind the window slide down behind the kept rows
+  (kara_compact_paged_tail), so no generated token escapes compression;
 * the compression itself is the three library calls on the due subset;
-  the freed blocks go back to the block allocator, and the sequence's length
-  becomes L + budget.
+  the freed blocks go back to the block allocator, the sequence's length
+  becomes base + budget + T, and its tail restarts at base + budget with the
+  T tokens that followed the window.
 
 Host objects: ``BlockAllocator`` (physical block ids shared by every layer),
 ``PagedCache`` (device pools, host block tables, per-sequence lengths) and
@@ -131,6 +135,7 @@ class PagedCache:
         self.alloc = BlockAllocator(num_blocks)
         self.tables = np.full((spec.num_seqs, max_blocks), -1, dtype=np.int32)
         self.lengths = np.zeros(spec.num_seqs, dtype=np.int64)
+        self.base = np.zeros(spec.num_seqs, dtype=np.int64)     # start of the never-compressed tail
         self.num_blocks, self.max_blocks = num_blocks, max_blocks
 
     def blocks_of(self, n: int) -> int:
@@ -168,6 +173,7 @@ class PagedCache:
         self.alloc.release(used.tolist())
         self.tables[n] = -1
         self.lengths[n] = 0
+        self.base[n] = 0
 
 
 def _config(spec: TraceSpec, num_seqs: int, cache: PagedCache):
@@ -178,15 +184,21 @@ def _config(spec: TraceSpec, num_seqs: int, cache: PagedCache):
 
 
 def compress(cache: PagedCache, seqs: list, q_windows: torch.Tensor, stream=None, record=None):
-    """Run score -> select -> compact on the subset `seqs` (windows = their
-    last `window` slots) and return the freed blocks to the allocator."""
+    """Run score -> select -> compact on the subset `seqs` (windows = the
+    oldest `window` tokens of their never-compressed tails, the newer tail
+    tokens sliding down behind the kept rows) and return the freed blocks to
+    the allocator."""
     s, dev = cache.spec, cache.device
     m = len(seqs)
     cfg = _config(s, m, cache)
     idx = np.asarray(seqs, dtype=np.int64)
-    prior = (cache.lengths[idx] - s.window).astype(np.int32)
+    prior = cache.base[idx].astype(np.int32)
+    tail = (cache.lengths[idx] - cache.base[idx] - s.window).astype(np.int32)
+    if (tail < 0).any():
+        raise ValueError("a due sequence holds less than one window of uncompressed tokens")
     tables = torch.from_numpy(cache.tables[idx]).to(dev)
     prior_t = torch.from_numpy(prior).to(dev)
+    tail_t = torch.from_numpy(tail).to(dev)
     scores = torch.empty((m, s.num_layers, s.num_kv_heads, s.window), dtype=torch.float32, device=dev)
     kept = torch.empty((m, s.num_layers, s.num_kv_heads, s.budget), dtype=torch.int32, device=dev)
     ws = torch.empty(K.kara_workspace_bytes(cfg) // 4 + 64, dtype=torch.float32, device=dev)
@@ -194,7 +206,8 @@ def compress(cache: PagedCache, seqs: list, q_windows: torch.Tensor, stream=None
     freed = torch.empty((m, K.kara_max_freed(cfg)), dtype=torch.int32, device=dev)
     nfreed = torch.empty(m, dtype=torch.int32, device=dev)
     if record is not None:
-        pre = dict(k=cache.k.clone(), v=cache.v.clone(), tables=cache.tables[idx].copy(), prior=prior.copy())
+        pre = dict(k=cache.k.clone(), v=cache.v.clone(), tables=cache.tables[idx].copy(), prior=prior.copy(),
+                   tail=tail.copy())
     # every window block must map to a physical block before the kernels use it
     bad = torch.full((1,), -1, dtype=torch.int32, device=dev)
     K.kara_validate_tables(cfg, tables, prior_t, bad, stream)
@@ -202,19 +215,20 @@ def compress(cache: PagedCache, seqs: list, q_windows: torch.Tensor, stream=None
         raise RuntimeError(f"scheduler: {int(bad.cpu().item())} due sequences have out-of-range block-table entries")
     K.kara_score_window(cfg, q_windows, cache.k, tables, prior_t, scores, ws, stream)
     K.kara_select_chunks(cfg, scores, kept, None, stream)
-    K.kara_compact_paged(cfg, cache.k, cache.v, tables, prior_t, seq_lens, kept, freed, nfreed, stream)
+    K.kara_compact_paged_tail(cfg, cache.k, cache.v, tables, prior_t, tail_t, seq_lens, kept, freed, nfreed, stream)
     new_tables = tables.cpu().numpy()
     fr, nf, sl = freed.cpu().numpy(), nfreed.cpu().numpy(), seq_lens.cpu().numpy()
     for i, n in enumerate(seqs):
         cache.tables[n] = new_tables[i]
         cache.alloc.release(fr[i, :nf[i]].tolist())
         cache.lengths[n] = int(sl[i])
+        cache.base[n] = int(prior[i]) + s.budget
     if record is not None:
         record.append(dict(seqs=list(seqs), q=q_windows.cpu(), scores=scores.cpu(), kept=kept.cpu(),
                            post_k=cache.k.cpu(), post_v=cache.v.cpu(), post_tables=cache.tables[idx].copy(),
                            seq_lens=sl.copy(), freed=[fr[i, :nf[i]].copy() for i in range(m)],
                            pre_k=pre["k"].cpu(), pre_v=pre["v"].cpu(), pre_tables=pre["tables"],
-                           prior=pre["prior"]))
+                           prior=pre["prior"], tail=pre["tail"]))
 
 
 def run_trace(spec: TraceSpec, device="cuda", compress_enabled=True, record=None, attention_every_tick=True):
@@ -240,6 +254,7 @@ def run_trace(spec: TraceSpec, device="cuda", compress_enabled=True, record=None
     t_compress = 0.0
     t_attn, attn_calls = 0.0, 0
     saved_samples = []
+    escaped_newest_window = 0
     st = torch.cuda.Stream(device=device)
     q_dec = None
     step = 0
@@ -253,6 +268,7 @@ def run_trace(spec: TraceSpec, device="cuda", compress_enabled=True, record=None
             if not active[n] and not done[n] and arrive[n] < nxt:
                 active[n] = True
                 items.append((n, int(prompt[n])))
+                cache.base[n] = int(prompt[n])          # the prompt is prior context, never compressed
         for n in range(S):
             if active[n]:
                 first = max(step, int(arrive[n]))
@@ -305,7 +321,12 @@ def run_trace(spec: TraceSpec, device="cuda", compress_enabled=True, record=None
                 t_compress += e[0].elapsed_time(e[1])
                 compressions += len(due)
                 for n in due:
-                    tails[n] = 0
+                    # the tokens behind the window stay in the (shorter) tail; had the
+                    # window been the newest W slots instead, they would have become
+                    # prior context and never been compressed
+                    behind = int(tails[n]) - spec.window
+                    escaped_newest_window += behind
+                    tails[n] = behind
         # finished sequences leave the batch and free their blocks
         for n in range(S):
             if active[n] and generated[n] >= gen[n]:
@@ -319,7 +340,11 @@ def run_trace(spec: TraceSpec, device="cuda", compress_enabled=True, record=None
             "blocks_peak": int(used_peak), "full_cache_blocks_peak": int(full_blocks_peak),
             "peak_saving": round(1.0 - used_peak / full_blocks_peak, 4) if full_blocks_peak else None,
             "mean_saving": round(float(np.mean(saved_samples)), 4) if saved_samples else None,
-            "blocks_in_use_at_end": cache.alloc.in_use}
+            "blocks_in_use_at_end": cache.alloc.in_use,
+            "tail_tokens_carried": int(escaped_newest_window),
+            "tail_tokens_carried_note": "tokens behind the compressed windows that stayed in the tail for a later "
+                                        "compression (with a window over the newest slots they would never have "
+                                        "been compressed)"}
 
 
 def main(argv=None):

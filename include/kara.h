@@ -170,6 +170,24 @@ int kara_compact_paged(const kara_config* cfg, void* k_cache, void* v_cache, int
                        int32_t* freed_blocks, int32_t* num_freed, void* stream);
 
 /*
+ * Step 3 when the window is the oldest part of the context not yet compressed
+ * (the gist.science explainer of the method, section "3. Der Periodische
+ * Zeitplan": the schedule cleans the back end of the current thought), so that
+ * tail_lens[n] = T newer tokens follow the window in slots [L+W, L+W+T).  Same
+ * as kara_compact_paged, except that after the kept rows those T rows move in
+ * order right behind them (slot L+B+t takes the old row of slot L+W+t), the
+ * table keeps the blocks of the first L+B+T slots (entries of logical blocks
+ * ceil((L+B+T)/bs) .. ceil((L+W+T)/bs)-1 are freed) and seq_lens[n] = L+B+T.
+ * tail_lens is int32 [num_seqs] device memory (required); a negative entry
+ * counts as 0, and T is clamped to the slots the table can address after the
+ * window.  T = 0 gives exactly kara_compact_paged.  Errors: KARA_EINVAL,
+ * KARA_ENULL, KARA_EHIP.
+ */
+int kara_compact_paged_tail(const kara_config* cfg, void* k_cache, void* v_cache, int32_t* block_tables,
+                            const int32_t* prior_lens, const int32_t* tail_lens, int32_t* seq_lens,
+                            const int32_t* kept, int32_t* freed_blocks, int32_t* num_freed, void* stream);
+
+/*
  * The whole step in one launch: scores, Token2Chunk selection and in-place
  * compaction of every unit, and every sequence's block-table rewrite, with
  * exactly the results of kara_score_window + kara_select_chunks +

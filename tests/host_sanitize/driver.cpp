@@ -124,12 +124,14 @@ int main() {
           EXPECT(kara_select_chunks(&c, fp, ip, bp, NULL), KARA_OK);
           EXPECT(kara_select_chunks_bridged(&c, 0, fp, ip, NULL, NULL), KARA_OK);
           EXPECT(kara_compact_paged(&c, p, p, ip, ip, ip, ip, ip, ip, NULL), KARA_OK);
+          EXPECT(kara_compact_paged_tail(&c, p, p, ip, ip, ip, ip, ip, ip, ip, NULL), KARA_OK);
+          EXPECT(kara_compact_paged_tail(&c, p, p, ip, ip, NULL, ip, ip, ip, ip, NULL), KARA_ENULL);
           EXPECT(kara_validate_tables(&c, ip, ip, ip, NULL), KARA_OK);
           EXPECT(kara_decode_attention(&c, p, p, p, ip, ip, fp, NULL, 0, NULL), KARA_OK);
           const int fused = kara_compress_fused_supported(&c);
           EXPECT(kara_compress_fused(&c, p, p, p, ip, ip, fp, ip, bp, ip, ip, ip, ip, NULL),
                  fused ? KARA_OK : KARA_ENOTIMPL);
-          calls += 6 + fused;
+          calls += 7 + fused;
         }
   EXPECT(g_launches, calls + 1 + 1);   // + the workspace and scratch-limit calls that reached a launcher
   for (int s = -8; s <= 2; ++s)

@@ -37,7 +37,7 @@ hipError_t launch_select(const Geo& g, int, const float*, int32_t*, uint8_t*, hi
   return hipSuccess;
 }
 hipError_t launch_compact(const Geo& g, int, void*, void*, int32_t*, const int32_t*, int32_t*, const int32_t*,
-                          int32_t*, int32_t*, int max_freed, hipStream_t) {
+                          int32_t*, int32_t*, int max_freed, const int32_t*, hipStream_t) {
   check_geo(g, "launch_compact");
   if (max_freed != (g.W + g.bs - 1) / g.bs + 1) abort();
   return hipSuccess;

@@ -1,7 +1,8 @@
 """Multi-round run of the periodic scheduler on the GPU path, every tick
 checked against the fp64 oracle applied to the cache as it was before that
 tick: scores within the score tolerance, kept lists, pools, block tables,
-lengths and freed blocks bit for bit."""
+lengths and freed blocks bit for bit.  The windows are the oldest uncompressed
+tokens, and the newer tokens behind them move down with the compaction."""
 import numpy as np
 import pytest
 import torch
@@ -23,6 +24,8 @@ def test_tiny_trace_every_tick_matches_the_oracle():
     rep = run_trace(spec, "cuda", record=rec)
     print(rep, flush=True)
     assert rep["compressions"] >= 4 and len(rec) >= 2
+    # the schedule really carries tails: some windows had newer tokens behind them
+    assert any(int(t) > 0 for r in rec for t in r["tail"])
     assert rep["blocks_in_use_at_end"] == 0
     assert rep["peak_saving"] > 0
     G = spec.num_q_heads // spec.num_kv_heads
@@ -40,7 +43,8 @@ def test_tiny_trace_every_tick_matches_the_oracle():
         ref = oracle.compress_step(np.zeros((len(r["seqs"]), spec.num_layers, spec.window, spec.num_q_heads, 1)),
                                    _bits(r["pre_k"]), _bits(r["pre_v"]), r["pre_tables"], r["prior"],
                                    window=spec.window, budget=spec.budget, seeds=spec.seeds, radius=spec.radius,
-                                   block_size=spec.block_size, scores_override=r["scores"].numpy())
+                                   block_size=spec.block_size, scores_override=r["scores"].numpy(),
+                                   tail_lens=r["tail"])
         assert np.array_equal(ref["kept"], r["kept"].numpy())
         assert np.array_equal(ref["k_pool"], _bits(r["post_k"]))
         assert np.array_equal(ref["v_pool"], _bits(r["post_v"]))
