@@ -3,8 +3,10 @@
 
 One step = kara_score_window + kara_select_chunks + kara_compact_paged over
 every (sequence, layer, KV head) of the workload, inputs resident in HBM.
-Between steps the window blocks and block tables are restored from a
-pristine copy (outside the timed events; compaction is in place).
+Between steps the blocks that compaction writes (those holding the slots
+[L, L+B) of each window) and the block tables are restored from a pristine
+copy (outside the timed events; compaction is in place), and once, before the
+timed steps, every window block is checked against that copy.
 
 After the timed steps, the consumer of the cache (one decode step of paged
 attention, kara_decode_attention) is timed over the compacted cache (L + B
@@ -179,15 +181,24 @@ def main():
     freed = torch.empty((S, K.kara_max_freed(cfg)), dtype=torch.int32, device=dev)
     nfreed = torch.empty(S, dtype=torch.int32, device=dev)
 
-    # pristine copy of every block a window touches, and of the tables
+    # pristine copy of every block a window touches, and of the tables.  A
+    # step writes only the slots [L, L+B) of each window (compaction), so the
+    # restore before each step copies back just the blocks that hold them; a
+    # check after the warm-up compares every window block with the copy.
     bs = shape.block_size
-    blocks = []
+    blocks, written = [], []
     for n in range(S):
         L = int(wl.host_prior_lens[n])
         blocks.extend(wl.host_tables[n, L // bs: -(-(L + W) // bs)].tolist())
+        written.extend(wl.host_tables[n, L // bs: -(-(L + B) // bs)].tolist())
     blk_idx = torch.tensor(blocks, dtype=torch.int64, device=dev)
     k_save = wl.k_pool.index_select(1, blk_idx)
     v_save = wl.v_pool.index_select(1, blk_idx)
+    pos_in_save = {b: i for i, b in enumerate(blocks)}
+    wr_idx = torch.tensor(written, dtype=torch.int64, device=dev)
+    wr_sel = torch.tensor([pos_in_save[b] for b in written], dtype=torch.int64, device=dev)
+    k_wsave = k_save.index_select(1, wr_sel)
+    v_wsave = v_save.index_select(1, wr_sel)
     tables_save = wl.block_tables.clone()
     # everything above ran on the default stream; the bench stream must not
     # start (restores read these copies) before it has finished
@@ -196,9 +207,17 @@ def main():
     st = torch.cuda.Stream(device=dev)
     def restore():
         with torch.cuda.stream(st):
-            wl.k_pool.index_copy_(1, blk_idx, k_save)
-            wl.v_pool.index_copy_(1, blk_idx, v_save)
+            wl.k_pool.index_copy_(1, wr_idx, k_wsave)
+            wl.v_pool.index_copy_(1, wr_idx, v_wsave)
             wl.block_tables.copy_(tables_save)
+
+    def pools_pristine():
+        """Every window block equals its pristine copy (after a restore)."""
+        with torch.cuda.stream(st):
+            ok = torch.equal(wl.k_pool.index_select(1, blk_idx), k_save) and \
+                torch.equal(wl.v_pool.index_select(1, blk_idx), v_save)
+        torch.cuda.synchronize()
+        return ok
 
     def step(e=None):
         if e:
@@ -239,7 +258,10 @@ def main():
     for _ in range(a.warmup):
         restore()
         step()
+    restore()
     torch.cuda.synchronize()
+    if not pools_pristine():
+        sys.exit("bench: a restore does not return the window blocks to their pristine contents")
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
     log(f"[bench] timing {a.steps} steps")
     torch.cuda.synchronize()
