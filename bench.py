@@ -52,6 +52,14 @@ def parse():
     return p.parse_args()
 
 
+def scorer_kernel(shape, passes: int) -> str:
+    """The kernel(s) kara_score_window launches for this shape."""
+    if passes == 2:
+        return "row_lse_kernel + col_mass_kernel"
+    resident = shape.dtype == "bf16" and shape.head_dim == 128 and shape.window <= 1024
+    return "fused_score_kernel" if resident else "small_score_kernel"
+
+
 def kernel_source_hash():
     from decode_kv_cache_amd.profiling import kernel_source_hash as h
     return h()
@@ -292,8 +300,7 @@ def main():
     khash = kernel_source_hash()
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": measured_traffic(shape.name, khash),
-            "kernel": ("fused_score_kernel" if K.kara_score_passes(cfg) == 1
-                       else "row_lse_kernel + col_mass_kernel") + " (kara_score_window)",
+            "kernel": scorer_kernel(shape, K.kara_score_passes(cfg)) + " (kara_score_window)",
             "algorithmic": f"2*G*W^2*d = {2 * G * W * W * d:.4g} FLOP per unit x {shape.units} units"}
     cbytes = 4.0 * B * d * shape.elem_bytes * shape.units
     t_c = float(np.mean(t_cmp)) / 1e3

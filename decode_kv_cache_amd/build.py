@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkara.so")
-SOURCES = ["api.hip", "score.hip", "score_fused.hip", "select.hip", "compact.hip", "decode_attn.hip"]
+SOURCES = ["api.hip", "score.hip", "score_fused.hip", "score_small.hip", "select.hip", "compact.hip",
+           "decode_attn.hip"]
 PROBES_LIB = os.path.join(PKG, "libkara_probes.so")
 PROBES_SOURCES = ["probes.hip"]
 

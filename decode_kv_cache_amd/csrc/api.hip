@@ -21,7 +21,12 @@ hipError_t launch_pipeline(const Geo& g, const void* q, void* kc, void* vc, int3
                            float* scores, int32_t* kept, uint8_t* mask, int32_t* seq_lens, int32_t* freed,
                            int32_t* num_freed, int max_freed, int32_t* done, hipStream_t st);
 int decode_attn_splits(const Geo& g);
-hipError_t launch_pipeline_noalloc(const Geo& g, const void* q, void* kc, void* vc, int32_t* tables,
+bool small_score_supported(const Geo& g, int dtype);
+bool pipeline_supported(const Geo& g, int dtype);
+hipError_t launch_pipeline_any(const Geo& g, int dtype, const void* q, void* kc, void* vc, int32_t* tables,
+                               const int32_t* prior, float* scores, int32_t* kept, uint8_t* mask, int32_t* seq_lens,
+                               int32_t* freed, int32_t* num_freed, int max_freed, int32_t* done, hipStream_t st);
+hipError_t launch_pipeline_noalloc(const Geo& g, int dtype, const void* q, void* kc, void* vc, int32_t* tables,
                                    const int32_t* prior, float* scores, int32_t* kept, uint8_t* mask,
                                    int32_t* seq_lens, int32_t* freed, int32_t* num_freed, int max_freed,
                                    hipStream_t st);
@@ -112,7 +117,8 @@ size_t kara_workspace_bytes(const kara_config* cfg) {
 
 int kara_score_passes(const kara_config* cfg) {
   if (check(cfg) != KARA_OK) return 0;
-  return kara::fused_score_supported(geo(cfg), cfg->dtype) ? 1 : 2;
+  const kara::Geo g = geo(cfg);
+  return kara::fused_score_supported(g, cfg->dtype) || kara::small_score_supported(g, cfg->dtype) ? 1 : 2;
 }
 
 int32_t kara_max_freed(const kara_config* cfg) {
@@ -163,7 +169,7 @@ int kara_select_chunks_bridged(const kara_config* cfg, int32_t gap, const float*
 
 int kara_compress_fused_supported(const kara_config* cfg) {
   if (check(cfg) != KARA_OK) return 0;
-  return kara::fused_score_supported(geo(cfg), cfg->dtype) ? 1 : 0;
+  return kara::pipeline_supported(geo(cfg), cfg->dtype) ? 1 : 0;
 }
 
 int kara_compress_fused(const kara_config* cfg, const void* q, void* k_cache, void* v_cache, int32_t* block_tables,
@@ -173,14 +179,14 @@ int kara_compress_fused(const kara_config* cfg, const void* q, void* k_cache, vo
   int s = check(cfg);
   if (s) return s;
   const kara::Geo g = geo(cfg);
-  if (!kara::fused_score_supported(g, cfg->dtype)) return KARA_ENOTIMPL;
+  if (!kara::pipeline_supported(g, cfg->dtype)) return KARA_ENOTIMPL;
   if (cfg->num_seqs == 0) return KARA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !prior_lens || !scores || !kept || !seq_lens || !freed_blocks ||
       !num_freed || !done)
     return KARA_ENULL;
-  return hip_status(kara::launch_pipeline(g, q, k_cache, v_cache, block_tables, prior_lens, scores, kept, mask,
-                                          seq_lens, freed_blocks, num_freed, kara_max_freed(cfg), done,
-                                          (hipStream_t)stream));
+  return hip_status(kara::launch_pipeline_any(g, cfg->dtype, q, k_cache, v_cache, block_tables, prior_lens, scores,
+                                              kept, mask, seq_lens, freed_blocks, num_freed, kara_max_freed(cfg),
+                                              done, (hipStream_t)stream));
 }
 
 int kara_compress_fused_noalloc(const kara_config* cfg, const void* q, void* k_cache, void* v_cache,
@@ -191,7 +197,7 @@ int kara_compress_fused_noalloc(const kara_config* cfg, const void* q, void* k_c
   int s = check(cfg);
   if (s) return s;
   const kara::Geo g = geo(cfg);
-  if (!kara::fused_score_supported(g, cfg->dtype)) return KARA_ENOTIMPL;
+  if (!kara::pipeline_supported(g, cfg->dtype)) return KARA_ENOTIMPL;
   if (cfg->num_seqs == 0) return KARA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !prior_lens || !scores || !kept || !seq_lens || !freed_blocks ||
       !num_freed)
@@ -203,7 +209,7 @@ int kara_compress_fused_noalloc(const kara_config* cfg, const void* q, void* k_c
       return KARA_EINVAL;
     if (cur != sdev) return KARA_EINVAL;
   }
-  return hip_status(kara::launch_pipeline_noalloc(g, q, k_cache, v_cache, block_tables, prior_lens, scores, kept,
+  return hip_status(kara::launch_pipeline_noalloc(g, cfg->dtype, q, k_cache, v_cache, block_tables, prior_lens, scores, kept,
                                                   mask, seq_lens, freed_blocks, num_freed, kara_max_freed(cfg),
                                                   (hipStream_t)stream));
 }

@@ -360,11 +360,16 @@ static hipError_t launch_score_t(const Geo& g, const void* q, const void* kc, co
 hipError_t launch_fused_score(const Geo& g, const void* q, const void* kc, const int32_t* tables,
                               const int32_t* prior, float* scores, hipStream_t st);
 bool fused_score_supported(const Geo& g, int dtype);
+bool small_score_supported(const Geo& g, int dtype);
+hipError_t launch_small_score(const Geo& g, int dtype, const void* q, const void* kc, const int32_t* tables,
+                              const int32_t* prior, float* scores, hipStream_t st);
 
 hipError_t launch_score(const Geo& g, int dtype, const void* q, const void* kc, const int32_t* tables,
                         const int32_t* prior, float* scores, float* ws, hipStream_t st) {
   // windows that fit in one workgroup's registers: single pass (score_fused.hip)
   if (fused_score_supported(g, dtype)) return launch_fused_score(g, q, kc, tables, prior, scores, st);
+  // small windows of the other element types and head_dims: single pass with K in LDS (score_small.hip)
+  if (small_score_supported(g, dtype)) return launch_small_score(g, dtype, q, kc, tables, prior, scores, st);
   if (dtype == KARA_BF16) {
     if (g.D == 128) return launch_score_t<__bf16, 128>(g, q, kc, tables, prior, scores, ws, st);
     return launch_score_t<__bf16, 64>(g, q, kc, tables, prior, scores, ws, st);
@@ -374,7 +379,7 @@ hipError_t launch_score(const Geo& g, int dtype, const void* q, const void* kc, 
 }
 
 size_t score_workspace_bytes(const Geo& g, int dtype) {
-  if (fused_score_supported(g, dtype)) return 0;
+  if (fused_score_supported(g, dtype) || small_score_supported(g, dtype)) return 0;
   return (size_t)g.S * g.Lyr * g.Hkv * (size_t)g.GWp * sizeof(float);
 }
 

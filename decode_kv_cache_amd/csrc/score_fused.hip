@@ -96,11 +96,12 @@ __device__ __forceinline__ void fused_unit(const Geo& g, int unit, const __bf16*
   // address is one scalar step per block; otherwise (and for a partial last
   // block) the row is split into (position, head) by division.
   const bool lin = (QB % g.G) == 0;
-  const int nfull = g.GW / QB;
+  const int nfull = lin ? g.GW / QB : 0;
   const long long lstep = lin ? (long long)(QB / g.G) * g.Hq * QROWB : 0;
-  const unsigned char* qlin = qbytes + ((long long)(srow / g.G) * g.Hq + srow % g.G) * QROWB + sbyte;
+  // the block's base address is uniform; a lane adds a 32-bit offset
+  const uint32_t qoff = (uint32_t)(((srow / g.G) * g.Hq + srow % g.G) * QROWB + sbyte);   // < 2^22
   auto q_fetch = [&](int b) -> uint2 {
-    if (lin && b < nfull) return *reinterpret_cast<const uint2*>(qlin + b * lstep);
+    if (b < nfull) return *reinterpret_cast<const uint2*>(qbytes + b * lstep + qoff);
     const int row = min(b * QB + srow, g.GW - 1);
     const int qi = row / g.G, qh = row - qi * g.G;
     return *reinterpret_cast<const uint2*>(qbytes + ((long long)qi * g.Hq + qh) * QROWB + sbyte);
@@ -402,7 +403,31 @@ hipError_t noalloc_scratch(int32_t** out) {
   return hipSuccess;
 }
 
-hipError_t launch_pipeline_noalloc(const Geo& g, const void* q, void* kc, void* vc, int32_t* tables,
+bool fused_score_supported(const Geo& g, int dtype);
+bool small_score_supported(const Geo& g, int dtype);
+hipError_t launch_small_pipeline(const Geo& g, int dtype, const void* q, void* kc, void* vc, int32_t* tables,
+                                 const int32_t* prior, float* scores, int32_t* kept, uint8_t* mask,
+                                 int32_t* seq_lens, int32_t* freed, int32_t* num_freed, int max_freed,
+                                 int32_t* done, hipStream_t st);
+
+// The one-launch step on whichever single-pass scorer covers the shape.
+hipError_t launch_pipeline_any(const Geo& g, int dtype, const void* q, void* kc, void* vc, int32_t* tables,
+                               const int32_t* prior, float* scores, int32_t* kept, uint8_t* mask, int32_t* seq_lens,
+                               int32_t* freed, int32_t* num_freed, int max_freed, int32_t* done, hipStream_t st) {
+  if (fused_score_supported(g, dtype))
+    return launch_pipeline(g, q, kc, vc, tables, prior, scores, kept, mask, seq_lens, freed, num_freed, max_freed,
+                           done, st);
+  if (small_score_supported(g, dtype))
+    return launch_small_pipeline(g, dtype, q, kc, vc, tables, prior, scores, kept, mask, seq_lens, freed, num_freed,
+                                 max_freed, done, st);
+  return hipErrorInvalidConfiguration;
+}
+
+bool pipeline_supported(const Geo& g, int dtype) {
+  return fused_score_supported(g, dtype) || small_score_supported(g, dtype);
+}
+
+hipError_t launch_pipeline_noalloc(const Geo& g, int dtype, const void* q, void* kc, void* vc, int32_t* tables,
                                    const int32_t* prior, float* scores, int32_t* kept, uint8_t* mask,
                                    int32_t* seq_lens, int32_t* freed, int32_t* num_freed, int max_freed,
                                    hipStream_t st) {
@@ -413,8 +438,8 @@ hipError_t launch_pipeline_noalloc(const Geo& g, const void* q, void* kc, void* 
   hipLaunchKernelGGL(zero_counters_kernel, dim3((g.S + 255) / 256), dim3(256), 0, st, done, g.S);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_pipeline(g, q, kc, vc, tables, prior, scores, kept, mask, seq_lens, freed, num_freed, max_freed,
-                         done, st);
+  return launch_pipeline_any(g, dtype, q, kc, vc, tables, prior, scores, kept, mask, seq_lens, freed, num_freed,
+                             max_freed, done, st);
 }
 
 bool fused_score_supported(const Geo& g, int dtype) {

@@ -99,10 +99,12 @@ int kara_check_config(const kara_config* cfg);
  * returns 0 for an invalid cfg. */
 size_t kara_workspace_bytes(const kara_config* cfg);
 
-/* Which scorer kara_score_window runs for cfg: 1 = single pass (bf16,
- * head_dim 128, W <= 1024: one workgroup per unit keeps the window's keys in
- * registers), 2 = two passes (row log-sum-exp, then column mass; needs the
- * workspace); 0 for an invalid cfg.  Both compute the same scores. */
+/* Which scorer kara_score_window runs for cfg: 1 = single pass, either with
+ * the window's keys resident in registers (bf16, head_dim 128, W <= 1024) or
+ * staged in LDS (any other dtype / head_dim with W <= 256, W <= 128 for fp32
+ * rows of head_dim 128); 2 = two passes (row log-sum-exp, then column mass;
+ * needs the workspace); 0 for an invalid cfg.  All compute the same scores.
+ * kara_workspace_bytes is 0 exactly when this is 1 (or cfg is invalid). */
 int kara_score_passes(const kara_config* cfg);
 
 /* Columns of freed_blocks: the most blocks one sequence can free, ceil(W/bs)+1. */
@@ -197,8 +199,8 @@ int kara_compact_paged_tail(const kara_config* cfg, void* k_cache, void* v_cache
  * sequence's table.  `done` is int32 [num_seqs] device memory that must hold
  * zeros before the first call; every call returns it to zeros.  Calls that
  * share a `done` array must not run concurrently.  Available when
- * kara_compress_fused_supported(cfg) is 1 (bf16, head_dim 128, W <= 1024),
- * else KARA_ENOTIMPL.  Other errors: KARA_EINVAL, KARA_ENULL, KARA_EHIP.
+ * kara_compress_fused_supported(cfg) is 1, which is exactly when
+ * kara_score_passes(cfg) is 1 (the single-pass scorers), else KARA_ENOTIMPL.  Other errors: KARA_EINVAL, KARA_ENULL, KARA_EHIP.
  */
 int kara_compress_fused_supported(const kara_config* cfg);
 

@@ -35,7 +35,7 @@ Readings taken where the pages are silent (each is stated where used):
   [p - radius, p + radius] clipped to the window; spans are merged; the rest
   of the budget goes to the best positions outside the spans, by the same
   order; exactly ``budget`` positions are kept, listed in ascending order.
-* R20     bridging variant (not the main rule): neighbouring seeds that leave
+* R31     bridging variant (not the main rule): neighbouring seeds that leave
   at most ``gap`` positions between them are joined by keeping everything in
   between (the lay explainers of KARA, part 2, describe keeping the tokens
   that lie between two important ones).
@@ -169,7 +169,7 @@ def chunk_bound(seeds, radius, gap):
 
 
 def token2chunk_bridge_select(scores, budget, seeds, radius, gap):
-    """Token2Chunk with bridging (variant; reading R20 of the lay explainers).
+    """Token2Chunk with bridging (variant; reading R31 of the lay explainers).
 
     The explainers of the method ([gist-de] section "2. Das Token2Chunk-Modul",
     and its Japanese twin) describe a chunk as everything lying between two

@@ -23,13 +23,22 @@ static void check_geo(const kara::Geo& g, const char* who) {
 
 namespace kara {
 bool fused_score_supported(const Geo& g, int dtype) { return dtype == KARA_BF16 && g.D == 128 && g.W <= 1024; }
+// staged-key scorer: 256 keys, 128 for fp32 rows of head_dim 128
+bool small_score_supported(const Geo& g, int dtype) {
+  if (fused_score_supported(g, dtype)) return false;
+  if (dtype == KARA_BF16) return g.D == 64 && g.W <= 256;
+  return g.W <= (g.D == 64 ? 256 : 128);
+}
+bool pipeline_supported(const Geo& g, int dtype) {
+  return fused_score_supported(g, dtype) || small_score_supported(g, dtype);
+}
 hipError_t launch_score(const Geo& g, int, const void*, const void*, const int32_t*, const int32_t*, float*, float*,
                         hipStream_t) {
   check_geo(g, "launch_score");
   return hipSuccess;
 }
 size_t score_workspace_bytes(const Geo& g, int dtype) {
-  if (fused_score_supported(g, dtype)) return 0;
+  if (pipeline_supported(g, dtype)) return 0;
   return (size_t)g.S * g.Lyr * g.Hkv * (size_t)g.GWp * sizeof(float);
 }
 hipError_t launch_select(const Geo& g, int, const float*, int32_t*, uint8_t*, hipStream_t) {
@@ -53,14 +62,16 @@ hipError_t launch_decode_attn(const Geo& g, int, const void*, const void*, const
   check_geo(g, "launch_decode_attn");
   return hipSuccess;
 }
-hipError_t launch_pipeline(const Geo& g, const void*, void*, void*, int32_t*, const int32_t*, float*, int32_t*,
-                           uint8_t*, int32_t*, int32_t*, int32_t*, int, int32_t*, hipStream_t) {
-  check_geo(g, "launch_pipeline");
+hipError_t launch_pipeline_any(const Geo& g, int dtype, const void*, void*, void*, int32_t*, const int32_t*, float*,
+                               int32_t*, uint8_t*, int32_t*, int32_t*, int32_t*, int, int32_t*, hipStream_t) {
+  check_geo(g, "launch_pipeline_any");
+  if (!pipeline_supported(g, dtype)) abort();
   return hipSuccess;
 }
-hipError_t launch_pipeline_noalloc(const Geo& g, const void*, void*, void*, int32_t*, const int32_t*, float*,
-                                   int32_t*, uint8_t*, int32_t*, int32_t*, int32_t*, int, hipStream_t) {
+hipError_t launch_pipeline_noalloc(const Geo& g, int dtype, const void*, void*, void*, int32_t*, const int32_t*,
+                                   float*, int32_t*, uint8_t*, int32_t*, int32_t*, int32_t*, int, hipStream_t) {
   check_geo(g, "launch_pipeline_noalloc");
+  if (!pipeline_supported(g, dtype)) abort();
   return hipSuccess;
 }
 }  // namespace kara

@@ -86,10 +86,20 @@ def test_workspace_bytes_and_max_freed():
     # two-pass scorer: one fp32 log-sum-exp per query row, rows padded to 32
     c1 = _cfg(window=2048)
     assert K.kara_workspace_bytes(c1) == units * 4 * 2048 * 4
-    c2 = _cfg(num_q_heads=28, num_kv_heads=4, window=33, budget=20, seeds=1, head_dim=64)   # G*W = 231 -> 256
-    assert K.kara_workspace_bytes(c2) == 64 * 32 * 4 * 256 * 4
+    c2 = _cfg(num_q_heads=28, num_kv_heads=4, window=300, budget=20, seeds=1, head_dim=64)  # G*W = 2100 -> 2112
+    assert K.kara_workspace_bytes(c2) == 64 * 32 * 4 * 2112 * 4
     c3 = _cfg(dtype=1)
     assert K.kara_workspace_bytes(c3) == units * 4 * 1024 * 4
+    # windows of at most 256 slots outside the resident-key scorer's shape: small single-pass scorer
+    small = [_cfg(num_q_heads=28, num_kv_heads=4, window=33, budget=20, seeds=1, head_dim=64),
+             _cfg(dtype=1, head_dim=64, window=256, budget=128),
+             _cfg(dtype=1, head_dim=128, window=128, budget=64, seeds=4, radius=2),
+             _cfg(head_dim=64, window=200, budget=100)]
+    for cs in small:
+        assert K.kara_workspace_bytes(cs) == 0 and K.kara_score_passes(cs) == 1
+    # fp32 rows of head_dim 128 stage at most 128 keys; a longer window takes two passes
+    assert K.kara_score_passes(_cfg(dtype=1, head_dim=128, window=129, budget=64, seeds=4, radius=2)) == 2
+    assert K.kara_score_passes(_cfg(dtype=1, head_dim=64, window=257, budget=64, seeds=4, radius=2)) == 2
     assert K.kara_max_freed(c) == 1024 // 16 + 1
     assert K.kara_max_freed(_cfg(window=100, budget=90, block_size=32)) == 4 + 1
     assert K.kara_workspace_bytes(_cfg(window=0)) == 0

@@ -56,6 +56,15 @@ SMALL = [
     # sixteen query heads per KV head
     KaraShape("g16", 117, num_seqs=2, num_layers=1, num_q_heads=16, num_kv_heads=1, head_dim=128,
               window=128, budget=30, seeds=3, radius=2, prior=("uniform", 10, 90), block_size=4),
+    # either side of the staged-key scorer's limits (256 keys; 128 for fp32 rows of head_dim 128)
+    KaraShape("f32_d128_w128_staged", 118, num_seqs=2, num_layers=1, num_q_heads=6, num_kv_heads=2, head_dim=128,
+              window=128, budget=32, seeds=2, radius=3, prior=("uniform", 0, 50), dtype="f32", plants=True),
+    KaraShape("f32_d128_w129_two_pass", 119, num_seqs=1, num_layers=1, num_q_heads=6, num_kv_heads=2, head_dim=128,
+              window=129, budget=32, seeds=2, radius=3, prior=("fixed", 11), dtype="f32", plants=True),
+    KaraShape("d64_g7_w255_staged", 120, num_seqs=2, num_layers=2, num_q_heads=14, num_kv_heads=2, head_dim=64,
+              window=255, budget=51, seeds=3, radius=3, prior=("uniform", 1, 99), key_model="outliers"),
+    KaraShape("f32_d64_w300_two_pass", 121, num_seqs=2, num_layers=1, num_q_heads=4, num_kv_heads=2, head_dim=64,
+              window=300, budget=60, seeds=3, radius=4, prior=("uniform", 0, 64), dtype="f32", block_size=8),
 ]
 
 
@@ -155,7 +164,7 @@ def test_validate_tables_flags_bad_sequences():
 
 def test_host_rejects_bad_arguments_before_enqueueing():
     from decode_kv_cache_amd import kara as K
-    wl = make_workload(SMALL[3], "cuda")      # head_dim 64: two-pass scorer with a workspace
+    wl = make_workload(SMALL[12], "cuda")     # W = 1500, head_dim 64: two-pass scorer with a workspace
     cfg = config_of(wl)
     out = Outputs(cfg, "cuda")
     small_ws = torch.empty(16, dtype=torch.float32, device="cuda")

@@ -1,4 +1,6 @@
-"""Single-launch pipeline (kara_compress_fused) against the three-call path and
+"""Single-launch pipeline (kara_compress_fused), with the resident-key scorer
+(bf16, head_dim 128, W <= 1024) and the staged-key scorer (other shapes, W up
+to 256, 128 for fp32 rows of head_dim 128), against the three-call path and
 the fp64 oracle: scores within the score tolerance of the oracle and equal to
 the three-call path's; kept lists, pools, block tables, lengths and freed
 blocks bit for bit; the done counters back to zero after every call."""
@@ -25,6 +27,17 @@ SHAPES = [
               window=1024, budget=204, seeds=8, radius=5, prior=("uniform", 0, 3000), plants=True),
     KaraShape("pipe_w1_keepall", 305, num_seqs=2, num_layers=1, num_q_heads=2, num_kv_heads=1, head_dim=128,
               window=33, budget=33, seeds=1, radius=0, prior=("fixed", 3), block_size=8),
+    # windows of at most 256 keys outside bf16 / head_dim 128: the staged-key scorer
+    shape_by_name("tiny"),
+    KaraShape("pipe_f32_d64_g7_w256", 306, num_seqs=3, num_layers=2, num_q_heads=7, num_kv_heads=1, head_dim=64,
+              window=256, budget=60, seeds=3, radius=4, dtype="f32", prior=("uniform", 0, 400), block_size=32,
+              plants=True),
+    KaraShape("pipe_bf16_d64_w200", 307, num_seqs=2, num_layers=2, num_q_heads=8, num_kv_heads=2, head_dim=64,
+              window=200, budget=50, seeds=4, radius=3, prior=("uniform", 10, 90), key_model="outliers"),
+    KaraShape("pipe_f32_d128_w128", 308, num_seqs=2, num_layers=1, num_q_heads=12, num_kv_heads=4, head_dim=128,
+              window=128, budget=40, seeds=2, radius=5, dtype="f32", prior=("fixed", 37), block_size=8),
+    KaraShape("pipe_f32_d64_w17", 309, num_seqs=3, num_layers=1, num_q_heads=3, num_kv_heads=1, head_dim=64,
+              window=17, budget=9, seeds=1, radius=2, dtype="f32", prior=("uniform", 0, 20), block_size=4),
 ]
 
 
@@ -91,7 +104,8 @@ def test_pipeline_twice_in_a_row_reuses_the_counters():
 
 
 def test_pipeline_not_offered_outside_its_shapes():
-    for s in (shape_by_name("tiny"), SHAPES[0].with_(head_dim=64), SHAPES[0].with_(window=2048, budget=410)):
+    for s in (SHAPES[0].with_(head_dim=64, window=300), SHAPES[0].with_(dtype="f32", window=129),
+              SHAPES[0].with_(dtype="f32", head_dim=64, window=257), SHAPES[0].with_(window=2048, budget=410)):
         wl = make_workload(s.with_(num_seqs=1), "cuda")
         cfg = config_of(wl)
         assert K.kara_compress_fused_supported(cfg) == 0

@@ -1,7 +1,7 @@
 """Selection on the GPU through exact ties.
 
 The Token2Chunk order compares scores as IEEE floats (-0 equals +0) and
-breaks ties by the lower position (reading R19 of the Kara abstract's
+breaks ties by the lower position (reading R30 of the Kara abstract's
 "select informative KV pairs ... expand a subset into chunks"), so the result
 is unique even when many scores are equal.  The radix selection takes the
 keys equal to a cutoff by ascending position; these tests put exact ties on

@@ -1,4 +1,4 @@
-"""Pins of the oracle's Token2Chunk bridging variant (reading R20).
+"""Pins of the oracle's Token2Chunk bridging variant (reading R31).
 
 Rule: seeds and their clipped radius spans as in the main Token2Chunk rule;
 seeds taken in ascending position; two neighbouring seeds p < p' that leave at

@@ -55,3 +55,15 @@ def test_noalloc_on_a_side_stream():
     print("[noalloc] side stream", flush=True)
     st = torch.cuda.Stream()
     _same(_run(SMALL, False), _run(SMALL, True, stream=st), "side stream")
+
+
+STAGED_BIG = KaraShape("noalloc_f32_d64", 963, num_seqs=4, num_layers=2, num_q_heads=6, num_kv_heads=2, head_dim=64,
+                       window=256, budget=64, seeds=2, radius=4, dtype="f32", prior=("uniform", 0, 70))
+STAGED_SMALL = KaraShape("noalloc_bf16_d64", 964, num_seqs=1, num_layers=1, num_q_heads=4, num_kv_heads=4,
+                         head_dim=64, window=40, budget=12, seeds=1, radius=2, prior=("fixed", 9), block_size=4)
+
+
+def test_noalloc_with_the_staged_key_scorer():
+    print("[noalloc] staged-key scorer shapes, big then smaller", flush=True)
+    _same(_run(STAGED_BIG, False), _run(STAGED_BIG, True), "first call")
+    _same(_run(STAGED_SMALL, False), _run(STAGED_SMALL, True), "second call, smaller batch")
