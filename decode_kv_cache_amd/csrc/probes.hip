@@ -198,6 +198,48 @@ __global__ __launch_bounds__(512, 1) void probe_coissue_cu(float* out, int iters
   out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// MFMA work and vector work in different waves of one SIMD: 512 threads with
+// 96 KiB of LDS (one workgroup per compute unit, two waves per SIMD); waves
+// 0-3 run NM independent MFMAs per iteration, waves 4-7 NV independent FMAs
+// (VK = 0) or bare v_exp_f32 (VK = 1).  Lane 0 of each wave writes
+// 1000 + 10 * (its SIMD from the HW_ID register) + (1 for a vector wave), so
+// the host can check that every SIMD holds one wave of each kind.
+template <int NM, int NV, int VK>
+__global__ __launch_bounds__(512, 1) void probe_split_cu(float* out, int iters, float a) {
+  extern __shared__ float lds_keep[];
+  const int wave = threadIdx.x >> 6;
+  const bool mfma_wave = wave < 4;
+  float s = 0.f;
+  if (mfma_wave) {
+    bf16x8 x[8], y;
+    for (int i = 0; i < 8; ++i) {
+      y[i] = (__bf16)(i * 1e-3f);
+      for (int m = 0; m < 8; ++m) x[m][i] = (__bf16)(threadIdx.x * 1e-3f + m);
+    }
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    f32x4 c[NM];
+    for (int m = 0; m < NM; ++m) c[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m) c[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x[m & 7], y, c[m], 0, 0, 0);
+    }
+    for (int m = 0; m < NM; ++m) s += c[m][0] + c[m][1] + c[m][2] + c[m][3];
+  } else {
+    float v[NV];
+    for (int e = 0; e < NV; ++e) v[e] = threadIdx.x * 1e-3f + e * 1e-2f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int e = 0; e < NV; ++e) v[e] = VK == 0 ? __builtin_fmaf(v[e], a, 0.5f) : __builtin_amdgcn_exp2f(-v[e]);
+    }
+    for (int e = 0; e < NV; ++e) s += v[e];
+  }
+  // HW_ID (hardware register 4), SIMD_ID field: bits 5:4
+  const int simd = (int)__builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4);
+  if (s == 12345.f) lds_keep[threadIdx.x] = s;   // the LDS allocation stays
+  out[blockIdx.x * blockDim.x + threadIdx.x] =
+      (threadIdx.x & 63) == 0 ? 1000.f + 10.f * simd + (mfma_wave ? 0.f : 1.f) : s;
+}
+
 static int status(hipError_t e) { return e == hipSuccess ? 0 : (int)e; }
 
 }  // namespace kara_probes
@@ -268,6 +310,12 @@ int kara_probe_coissue_cu(int mode, float* out, int blocks, int threads, int ite
     case 4: hipLaunchKernelGGL((probe_coissue_cu<16, 64, 0, 1>), g, b, lds, st, out, iters, 0.999f); break;
     case 5: hipLaunchKernelGGL((probe_coissue_cu<0, 32, 1, 0>), g, b, lds, st, out, iters, 0.999f); break;
     case 6: hipLaunchKernelGGL((probe_coissue_cu<16, 32, 1, 1>), g, b, lds, st, out, iters, 0.999f); break;
+    case 7:
+    case 8:
+      if (threads != 512) return -1;
+      if (mode == 7) hipLaunchKernelGGL((probe_split_cu<16, 64, 0>), g, b, lds, st, out, iters, 0.999f);
+      else hipLaunchKernelGGL((probe_split_cu<16, 32, 1>), g, b, lds, st, out, iters, 0.999f);
+      break;
     default: return -1;
   }
   return status(hipGetLastError());

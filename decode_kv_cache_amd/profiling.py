@@ -354,6 +354,22 @@ def cmd_coissue_cu(a):
             torch.cuda.synchronize()
             row.append(ev[0].elapsed_time(ev[1]) * 1e6 / a.iters / (threads // 256))
         print(f"| {name} | {row[0]:.1f} ns | {row[1]:.1f} ns |", flush=True)
+    # the MFMAs and the vector work in the two different waves of each SIMD
+    print()
+    print("| Waves 0-3 / waves 4-7 of each workgroup (2 per SIMD) | Time per iteration | Waves placed one of each kind per SIMD |")
+    print("|---|---|---|")
+    for mode, name in ((7, "16 MFMA / 64 FMA"), (8, "16 MFMA / 32 v_exp_f32")):
+        if lib.kara_probe_coissue_cu(mode, o, cus, 512, 10, sp) != 0:
+            raise RuntimeError("probe launch failed")
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(st)
+        lib.kara_probe_coissue_cu(mode, o, cus, 512, a.iters, sp)
+        ev[1].record(st)
+        torch.cuda.synchronize()
+        tags = out.view(cus, 8, 64)[:, :, 0].cpu().numpy().astype(int) - 1000
+        ok = all(sorted(t.tolist()) == [0, 1, 10, 11, 20, 21, 30, 31] for t in tags)
+        print(f"| {name} | {ev[0].elapsed_time(ev[1]) * 1e6 / a.iters:.1f} ns | {'yes' if ok else 'no'} |",
+              flush=True)
 
 
 def cmd_compact_patterns(a):

@@ -41,6 +41,9 @@ int kara_probe_coissue(int mode, float* out, int blocks, int threads, int iters,
  * mode 0: 16 independent 16x16x32 bf16 MFMAs; mode 1: 64 independent fp32 FMAs;
  * modes 2, 3, 4: the 16 MFMAs with 16, 32 or 64 FMAs interleaved (MFMA, 1/2/4 FMAs, ...);
  * mode 5: 32 bare v_exp_f32; mode 6: the 16 MFMAs with the 32 v_exp_f32 interleaved.
+ * Modes 7 and 8 (threads = 512 only) split the work between the two waves of each SIMD:
+ * waves 0-3 run 16 MFMAs per iteration, waves 4-7 run 64 FMAs (mode 7) or 32 bare
+ * v_exp_f32 (mode 8); lane 0 of each wave writes 1000 + 10 * SIMD id + (1 for a vector wave).
  * out: blocks * threads floats. */
 int kara_probe_coissue_cu(int mode, float* out, int blocks, int threads, int iters, void* stream);
 
