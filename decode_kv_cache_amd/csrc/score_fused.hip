@@ -71,7 +71,7 @@ __device__ __forceinline__ float group_sum(float v) {
 //     m = max_w m_w,   l = sum_w l_w 2^(alpha (m_w - m)),
 // and weights its exponentials by 2^(alpha (m_w - m)) / l, which is the
 // softmax over all W keys of the row.
-template <bool MASK>
+template <bool MASK, bool LIN>
 __device__ __forceinline__ void fused_unit(const Geo& g, int unit, const __bf16* __restrict__ q,
                                            const bf16x8 (&kf)[KTW][4], int key0, unsigned char (*qtile)[QB * QLROW],
                                            float2 (*red)[QB][FW], float* __restrict__ scores,
@@ -91,17 +91,15 @@ __device__ __forceinline__ void fused_unit(const Geo& g, int unit, const __bf16*
   // staging: the 512 threads move 16 rows x 256 bytes, 8 bytes each; tiles are
   // fetched two blocks ahead (two register stages) to cover memory latency
   const int srow = tid >> 5, sbyte = (tid & 31) * 8;
-  // When G divides the block height, a thread's row of block b sits at a
-  // fixed offset plus b times the bytes of QB / G window positions, so the
-  // address is one scalar step per block; otherwise (and for a partial last
-  // block) the row is split into (position, head) by division.
-  const bool lin = (QB % g.G) == 0;
-  const int nfull = lin ? g.GW / QB : 0;
-  const long long lstep = lin ? (long long)(QB / g.G) * g.Hq * QROWB : 0;
-  // the block's base address is uniform; a lane adds a 32-bit offset
+  // LIN (G divides the block height and every block is full): a thread's row
+  // of block b sits at a fixed offset plus b times the bytes of QB / G window
+  // positions, so the block's base address is one scalar step and a lane adds
+  // a 32-bit offset: no vector arithmetic per block.  Otherwise the row is
+  // split into (position, head) by division.
+  const long long lstep = (long long)(QB / g.G) * g.Hq * QROWB;
   const uint32_t qoff = (uint32_t)(((srow / g.G) * g.Hq + srow % g.G) * QROWB + sbyte);   // < 2^22
   auto q_fetch = [&](int b) -> uint2 {
-    if (b < nfull) return *reinterpret_cast<const uint2*>(qbytes + b * lstep + qoff);
+    if (LIN) return *reinterpret_cast<const uint2*>(qbytes + b * lstep + qoff);
     const int row = min(b * QB + srow, g.GW - 1);
     const int qi = row / g.G, qh = row - qi * g.G;
     return *reinterpret_cast<const uint2*>(qbytes + ((long long)qi * g.Hq + qh) * QROWB + sbyte);
@@ -190,7 +188,7 @@ __device__ __forceinline__ void fused_unit(const Geo& g, int unit, const __bf16*
     const float l = group_sum(pp.y * fast_exp2(pp.x - m) + pp.w * fast_exp2(pp.z - m));   // m_w = -inf -> 0
     // this wave's weight; rows past G*W contribute nothing
     const float own = MASK && mx == -INFINITY ? 0.f : fast_exp2(ma - m);
-    const float wgt = (b * QB + qlane < g.GW) ? own * __builtin_amdgcn_rcpf(l) : 0.f;
+    const float wgt = (LIN || b * QB + qlane < g.GW) ? own * __builtin_amdgcn_rcpf(l) : 0.f;
 #pragma unroll
     for (int t = 0; t < KTW; ++t)
 #pragma unroll
@@ -230,6 +228,23 @@ __device__ __forceinline__ void fused_unit(const Geo& g, int unit, const __bf16*
     }
 }
 
+// Every wave of the workgroup takes the same branch: it depends on the
+// geometry only.  MASK: the window is shorter than the 8 waves' 1024 keys.
+__device__ __forceinline__ void fused_unit_any(const Geo& g, int unit, const __bf16* __restrict__ q,
+                                               const bf16x8 (&kf)[KTW][4], int key0,
+                                               unsigned char (*qtile)[QB * QLROW], float2 (*red)[QB][FW],
+                                               float* __restrict__ scores, uint32_t* keys_lds) {
+  const bool mask = g.W < FW * KTW * 16;
+  const bool lin = QB % g.G == 0 && g.GW % QB == 0;
+  if (mask) {
+    if (lin) fused_unit<true, true>(g, unit, q, kf, key0, qtile, red, scores, keys_lds);
+    else fused_unit<true, false>(g, unit, q, kf, key0, qtile, red, scores, keys_lds);
+  } else {
+    if (lin) fused_unit<false, true>(g, unit, q, kf, key0, qtile, red, scores, keys_lds);
+    else fused_unit<false, false>(g, unit, q, kf, key0, qtile, red, scores, keys_lds);
+  }
+}
+
 __global__ __launch_bounds__(FTHREADS, 1) void fused_score_kernel(Geo g, const __bf16* __restrict__ q,
                                                                    const __bf16* __restrict__ kc,
                                                                    const int32_t* __restrict__ tables,
@@ -262,11 +277,7 @@ __global__ __launch_bounds__(FTHREADS, 1) void fused_score_kernel(Geo g, const _
       __builtin_memcpy(&kf[t][s], &v, 16);
     }
   }
-  // every wave of the workgroup takes the same branch (it depends on W only)
-  if (g.W >= FW * KTW * 16)
-    fused_unit<false>(g, unit, q, kf, key0, qtile, red, scores, nullptr);
-  else
-    fused_unit<true>(g, unit, q, kf, key0, qtile, red, scores, nullptr);
+  fused_unit_any(g, unit, q, kf, key0, qtile, red, scores, nullptr);
 }
 
 hipError_t launch_fused_score(const Geo& g, const void* q, const void* kc, const int32_t* tables,
@@ -329,10 +340,7 @@ __global__ __launch_bounds__(FTHREADS, 1) void pipeline_kernel(Geo g, const __bf
         __builtin_memcpy(&kf[t][s], &v, 16);
       }
     }
-    if (g.W >= FW * KTW * 16)
-      fused_unit<false>(g, unit, q, kf, key0, qtile, red, scores, keys);
-    else
-      fused_unit<true>(g, unit, q, kf, key0, qtile, red, scores, keys);
+    fused_unit_any(g, unit, q, kf, key0, qtile, red, scores, keys);
   }
   select_unit<FTHREADS, FW * KTW * 16 / FTHREADS>(g, 0, keys, flags, sh, kl, kept + (long long)unit * g.B,
                         mask ? mask + (long long)unit * g.W : nullptr);
