@@ -21,7 +21,9 @@
  *
  * Conventions for every entry point
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library
- *    allocates nothing, keeps no state between calls and is reentrant.
+ *    allocates nothing, keeps no state between calls and is reentrant, apart
+ *    from kara_compress_fused_noalloc's fixed per-device counter array (see
+ *    there).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
  *    work and return; results are ready when the stream reaches them.
  *  - Arguments are checked on the host before anything is enqueued: a call that
