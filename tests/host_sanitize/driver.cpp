@@ -1,14 +1,18 @@
 // Drives every entry point of the C ABI through its host-side checks: invalid
 // and extreme configurations, NULL and fake pointers on the rejection paths,
-// and valid calls over many geometries that reach the (stand-in) launchers.
+// valid calls over many geometries that reach the (stand-in) launchers, and
+// launches the stand-in runtime refuses (KARA_EHIP).
 // Exit status 0 when every returned status is the documented one.
 #include <limits.h>
 #include <stdio.h>
 #include <string.h>
 
+#include <hip/hip_runtime_api.h>
+
 #include "kara.h"
 
 extern int g_launches;
+extern int g_fail_launch;
 static int fails = 0;
 
 #define EXPECT(expr, want)                                                          \
@@ -134,6 +138,25 @@ int main() {
           calls += 7 + fused;
         }
   EXPECT(g_launches, calls + 1 + 1);   // + the workspace and scratch-limit calls that reached a launcher
+  // a launch the runtime refuses comes back as KARA_EHIP with the HIP code kept for kara_last_hip_error
+  {
+    kara_config c = base();
+    g_fail_launch = 1;
+    EXPECT(kara_last_hip_error(), 0);
+    EXPECT(kara_score_window(&c, p, p, ip, ip, fp, NULL, 0, NULL), KARA_EHIP);
+    EXPECT(kara_last_hip_error(), hipErrorLaunchFailure);
+    EXPECT(kara_select_chunks(&c, fp, ip, bp, NULL), KARA_EHIP);
+    EXPECT(kara_select_chunks_bridged(&c, 0, fp, ip, NULL, NULL), KARA_EHIP);
+    EXPECT(kara_compact_paged(&c, p, p, ip, ip, ip, ip, ip, ip, NULL), KARA_EHIP);
+    EXPECT(kara_compact_paged_tail(&c, p, p, ip, ip, ip, ip, ip, ip, ip, NULL), KARA_EHIP);
+    EXPECT(kara_validate_tables(&c, ip, ip, ip, NULL), KARA_EHIP);
+    EXPECT(kara_decode_attention(&c, p, p, p, ip, ip, fp, NULL, 0, NULL), KARA_EHIP);
+    EXPECT(kara_compress_fused(&c, p, p, p, ip, ip, fp, ip, bp, ip, ip, ip, ip, NULL), KARA_EHIP);
+    EXPECT(kara_compress_fused_noalloc(&c, p, p, p, ip, ip, fp, ip, bp, ip, ip, ip, NULL), KARA_EHIP);
+    EXPECT(kara_last_hip_error(), hipErrorLaunchFailure);
+    EXPECT(g_launches, calls + 1 + 1);   // nothing counted as launched
+    g_fail_launch = 0;
+  }
   for (int s = -8; s <= 2; ++s)
     if (!kara_status_str(s) || !strlen(kara_status_str(s))) ++fails;
   printf("host checks: %d launches, %d failures\n", g_launches, fails);

@@ -1,7 +1,8 @@
 // Host-only stand-ins for the kernel launchers and the few runtime calls the
 // C ABI makes, so that the ABI's argument checks and geometry can run under
 // AddressSanitizer and UndefinedBehaviorSanitizer on a machine without a GPU.
-// Every launcher checks the geometry it receives and counts the call.
+// Every launcher checks the geometry it receives and counts the call, or,
+// while g_fail_launch is set, reports a launch failure as the runtime would.
 #include <math.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -9,6 +10,7 @@
 #include "kara_device.h"
 
 int g_launches = 0;
+int g_fail_launch = 0;   // when set, every launcher reports a launch failure without counting a launch
 
 static void check_geo(const kara::Geo& g, const char* who) {
   const bool ok = g.S >= 1 && g.Lyr >= 1 && g.Hkv >= 1 && g.G >= 1 && g.Hq == g.G * g.Hkv && g.GW == g.G * g.W &&
@@ -34,6 +36,7 @@ bool pipeline_supported(const Geo& g, int dtype) {
 }
 hipError_t launch_score(const Geo& g, int, const void*, const void*, const int32_t*, const int32_t*, float*, float*,
                         hipStream_t) {
+  if (g_fail_launch) return hipErrorLaunchFailure;
   check_geo(g, "launch_score");
   return hipSuccess;
 }
@@ -42,16 +45,19 @@ size_t score_workspace_bytes(const Geo& g, int dtype) {
   return (size_t)g.S * g.Lyr * g.Hkv * (size_t)g.GWp * sizeof(float);
 }
 hipError_t launch_select(const Geo& g, int, const float*, int32_t*, uint8_t*, hipStream_t) {
+  if (g_fail_launch) return hipErrorLaunchFailure;
   check_geo(g, "launch_select");
   return hipSuccess;
 }
 hipError_t launch_compact(const Geo& g, int, void*, void*, int32_t*, const int32_t*, int32_t*, const int32_t*,
                           int32_t*, int32_t*, int max_freed, const int32_t*, hipStream_t) {
+  if (g_fail_launch) return hipErrorLaunchFailure;
   check_geo(g, "launch_compact");
   if (max_freed != (g.W + g.bs - 1) / g.bs + 1) abort();
   return hipSuccess;
 }
 hipError_t launch_validate(const Geo& g, const int32_t*, const int32_t*, int32_t*, hipStream_t) {
+  if (g_fail_launch) return hipErrorLaunchFailure;
   check_geo(g, "launch_validate");
   return hipSuccess;
 }
@@ -59,17 +65,20 @@ size_t decode_attn_workspace_bytes(const Geo&) { return 0; }
 int decode_attn_splits(const Geo&) { return 1; }
 hipError_t launch_decode_attn(const Geo& g, int, const void*, const void*, const void*, const int32_t*,
                               const int32_t*, float*, float*, hipStream_t) {
+  if (g_fail_launch) return hipErrorLaunchFailure;
   check_geo(g, "launch_decode_attn");
   return hipSuccess;
 }
 hipError_t launch_pipeline_any(const Geo& g, int dtype, const void*, void*, void*, int32_t*, const int32_t*, float*,
                                int32_t*, uint8_t*, int32_t*, int32_t*, int32_t*, int, int32_t*, hipStream_t) {
+  if (g_fail_launch) return hipErrorLaunchFailure;
   check_geo(g, "launch_pipeline_any");
   if (!pipeline_supported(g, dtype)) abort();
   return hipSuccess;
 }
 hipError_t launch_pipeline_noalloc(const Geo& g, int dtype, const void*, void*, void*, int32_t*, const int32_t*,
                                    float*, int32_t*, uint8_t*, int32_t*, int32_t*, int32_t*, int, hipStream_t) {
+  if (g_fail_launch) return hipErrorLaunchFailure;
   check_geo(g, "launch_pipeline_noalloc");
   if (!pipeline_supported(g, dtype)) abort();
   return hipSuccess;

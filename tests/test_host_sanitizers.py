@@ -4,9 +4,11 @@ AddressSanitizer and UndefinedBehaviorSanitizer, on the CPU.
 api.hip is compiled for the host only, with the sanitizers, and linked with
 stand-ins for the kernel launchers (tests/host_sanitize/stubs.cpp) and a
 driver (tests/host_sanitize/driver.cpp) that sends every entry point invalid
-and extreme configurations, NULL and fake pointers on the rejection paths, and
-valid calls over many geometries.  The program must report every status as
-documented and the sanitizers must stay silent.  No GPU code is built or run.
+and extreme configurations, NULL and fake pointers on the rejection paths,
+valid calls over many geometries, and calls whose launch the (stand-in)
+runtime refuses, which must come back as KARA_EHIP with the HIP code kept for
+kara_last_hip_error.  The program must report every status as documented and
+the sanitizers must stay silent.  No GPU code is built or run.
 """
 import os
 import shutil
