@@ -52,6 +52,19 @@ def parse():
     return p.parse_args()
 
 
+def run_environment(dev) -> dict:
+    """What the line was measured on: GPU, its compute units and clock, the
+    HIP runtime and torch builds, the library's source hash."""
+    import torch
+    p = torch.cuda.get_device_properties(dev)
+    env = {"gpu": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+           "hip": torch.version.hip, "torch": torch.__version__}
+    clock = getattr(p, "clock_rate", None)
+    if clock:
+        env["max_clock_mhz"] = round(clock / 1000.0)
+    return env
+
+
 def scorer_kernel(shape, passes: int) -> str:
     """The kernel(s) kara_score_window launches for this shape."""
     if passes == 2:
@@ -444,6 +457,7 @@ def main():
         "achievable_peaks": achievable,
         "kernel_hash": khash,
         "wall_ms_per_step_incl_restore": round(wall / a.steps * 1e3, 3),
+        "env": run_environment(dev),
     }
     print(json.dumps(out), flush=True)
 
