@@ -284,7 +284,7 @@ const char* kara_status_str(int status) {
     case KARA_ENULL: return "required pointer is NULL";
     case KARA_EWORKSPACE: return "workspace missing, misaligned or too small";
     case KARA_EHIP: return "HIP runtime error while enqueueing";
-    case KARA_ENOTIMPL: return "not supported by this build";
+    case KARA_ENOTIMPL: return "valid request this library does not support";
     case KARA_ESCRATCH: return "more sequences than the fixed scratch of an allocation-free entry point holds";
     default: return "unknown status";
   }

@@ -37,12 +37,14 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def kernel_source_hash() -> str:
-    """Hash of every library kernel source (the probes are tools, not part of
-    it); a stored measurement is valid for this hash only."""
+    """Hash of every source that goes into the library's kernels: all of csrc
+    but the host-only ABI layer (api.hip, no device code) and the probes
+    (tools, not part of the library).  A stored measurement is valid for this
+    hash only."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "decode_kv_cache_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        if f == "probes.hip":
+        if f in ("probes.hip", "api.hip"):
             continue
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())

@@ -68,7 +68,7 @@ extern "C" {
 #define KARA_ENULL (-2)      /* a required pointer is NULL */
 #define KARA_EWORKSPACE (-3) /* workspace missing or smaller than kara_workspace_bytes */
 #define KARA_EHIP (-4)       /* the HIP runtime reported an error while enqueueing */
-#define KARA_ENOTIMPL (-5)   /* valid request this build does not support */
+#define KARA_ENOTIMPL (-5)   /* valid request this library does not support */
 #define KARA_ESCRATCH (-6)   /* request larger than the fixed scratch of an allocation-free entry point */
 
 /* most sequences one kara_compress_fused_noalloc call may cover */
