@@ -67,3 +67,38 @@ def test_noalloc_with_the_staged_key_scorer():
     print("[noalloc] staged-key scorer shapes, big then smaller", flush=True)
     _same(_run(STAGED_BIG, False), _run(STAGED_BIG, True), "first call")
     _same(_run(STAGED_SMALL, False), _run(STAGED_SMALL, True), "second call, smaller batch")
+
+
+def test_noalloc_replayed_from_a_captured_graph():
+    """Code under graph capture is one of the callers the entry point is for:
+    the call is captured once on a side stream and the graph is replayed three
+    times, with eager copies restoring the inputs and refilling the outputs
+    between replays; every replay gives the eager call's results bit for bit.
+    The counters are cleared by a kernel, so the graph holds no memset node."""
+    print("[noalloc] graph capture and three replays", flush=True)
+    ref = _run(SMALL, True)            # eager result; also looks up the per-device counter array
+    wl = make_workload(SMALL, "cuda")
+    cfg = config_of(wl)
+    out = Outputs(cfg, "cuda")
+    k0, v0, t0 = wl.k_pool.clone(), wl.v_pool.clone(), wl.block_tables.clone()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.graph(graph, stream=side):
+        K.kara_compress_fused_noalloc(cfg, wl.q, wl.k_pool, wl.v_pool, wl.block_tables, wl.prior_lens,
+                                      out["scores"], out["kept"], out["seq_lens"], out["freed"], out["num_freed"],
+                                      mask=out["mask"])
+    torch.cuda.synchronize()
+    for i in range(3):
+        wl.k_pool.copy_(k0)
+        wl.v_pool.copy_(v0)
+        wl.block_tables.copy_(t0)
+        for k, buf in out.raw.items():
+            buf.fill_(out.fill[k])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert out.guards_intact()
+        res = {k: bits(out[k]) for k in ("scores", "kept", "mask", "seq_lens", "freed", "num_freed")}
+        res.update(k=bits(wl.k_pool), v=bits(wl.v_pool), tables=wl.block_tables.cpu().numpy())
+        _same(ref, res, f"replay {i}")
