@@ -66,3 +66,33 @@ def test_random_configuration(i):
     freed = out["freed"].cpu().numpy()
     for n in range(s.num_seqs):
         assert freed[n, :int(ref["num_freed"][n])].tolist() == ref["freed"][n].tolist()
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_configuration_one_launch(i):
+    """The same configurations through kara_compress_fused, where it is
+    offered (a single-pass scorer runs): every output, pool byte and table
+    equal to the three calls' bit for bit (reading R29)."""
+    import torch
+
+    from decode_kv_cache_amd import kara as K
+    from tests.kara_harness import Outputs, config_of
+    s, _ = _random_shape(i)
+    wa = make_workload(s, "cuda")
+    cfg = config_of(wa)
+    if not K.kara_compress_fused_supported(cfg):
+        pytest.skip("two-pass scorer shape: the one-launch pipeline is not offered")
+    wb = make_workload(s, "cuda")
+    _, ref = run_step(wa, cfg)
+    out = Outputs(cfg, "cuda")
+    done = torch.zeros(s.num_seqs, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    K.kara_compress_fused(cfg, wb.q, wb.k_pool, wb.v_pool, wb.block_tables, wb.prior_lens, out["scores"],
+                          out["kept"], out["seq_lens"], out["freed"], out["num_freed"], done, mask=out["mask"])
+    torch.cuda.synchronize()
+    assert out.guards_intact() and bool((done == 0).all())
+    for k in ("scores", "kept", "mask", "seq_lens", "num_freed", "freed"):
+        assert np.array_equal(bits(out[k]), bits(ref[k])), (s.name, k)
+    assert np.array_equal(bits(wb.k_pool), bits(wa.k_pool))
+    assert np.array_equal(bits(wb.v_pool), bits(wa.v_pool))
+    assert torch.equal(wb.block_tables, wa.block_tables)
