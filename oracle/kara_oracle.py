@@ -50,7 +50,25 @@ Readings taken where the pages are silent (each is stated where used):
   the current thought), the newer tokens behind it move down, in order,
   right after the kept rows.
 
-Parity pins for each function live in ``tests/test_oracle_*.py``.
+Parity pins (``tests/test_oracle_*.py``; every function has at least one,
+none is parity unpinned):
+
+* window_scores            closed forms (tests/golden/scores_hand.json), the
+                           W = 2 logistic, hard-softmax limits, invariants
+                           (sum = G*W, identical keys), planted keys, mutants;
+* token2chunk_select       hand cases and brute force over tiny windows;
+* token2chunk_bridge_select, chunk_bound
+                           hand cases (tests/golden/select_bridge_hand.json), a
+                           per-position definition, exhaustive placements;
+* gather_window_rows, compact_window_rows, compact_paged_sequence,
+  rewrite_block_table      a hand-worked case, a naive slot-by-slot gather,
+                           the closed-form freed count, with and without a tail
+                           (tests/golden/compact_tail_hand.json), mutants;
+* paged_decode_attention   closed forms, torch's attention on gathered rows,
+                           invariances, mutants;
+* batch_unit_scores, compress_step
+                           per-unit closed forms that differ by head, layer,
+                           sequence and window start, with mutants of each.
 """
 
 from __future__ import annotations
