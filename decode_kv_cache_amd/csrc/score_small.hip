@@ -8,15 +8,17 @@
 //
 // For windows of at most 256 keys whose K rows fit in 72 KiB of LDS (128
 // keys for fp32 rows of head_dim 128), in the shapes the resident-key scorer
-// in score_fused.hip does not take: fp32, or head_dim 64.  One workgroup of 4 waves owns one unit and stages the
-// window's K rows in LDS once.  Each wave takes every fourth block of 16
-// query rows and computes the block's logits against all W keys with 16x16
-// MFMAs in the transposed orientation S^T = K Q^T (a lane owns one query row
-// and 4 keys of every 16-key tile), so each row's max and sum are complete in
-// the wave: no exchange between waves and no barrier inside the loop.  The
-// softmax weights are exact fp32 exponentials over the row's sum; the column
-// sums accumulate per lane, are reduced over the 16 query lanes and then over
-// the 4 waves in a fixed order.  Each logit is computed once.
+// in score_fused.hip does not take: fp32, or head_dim 64.  One workgroup of
+// 4 waves owns one unit and stages the window's K rows in LDS once.  Each
+// wave takes every fourth block of 16 query rows and computes the block's
+// logits against all W keys with 16x16 MFMAs (16x16x32 bf16, 16x16x4 fp32)
+// in the transposed orientation S^T = K Q^T (a lane owns one query row and 4
+// keys of every 16-key tile), so each row's max and sum are complete in the
+// wave: no exchange between waves and no barrier inside the loop.  The
+// softmax weights are fp32 exponentials over the row's fp32 sum (no fp16
+// rounding anywhere); the column sums accumulate per lane, are reduced over
+// the 16 query lanes and then over the 4 waves in a fixed order.  Each logit
+// is computed once.
 #include "compact_core.h"
 #include "kara_device.h"
 #include "select_core.h"

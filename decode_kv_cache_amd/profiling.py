@@ -36,18 +36,51 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def kernel_source_hash() -> str:
-    """Hash of every source that goes into the library's kernels: all of csrc
-    but the host-only ABI layer (api.hip, no device code) and the probes
-    (tools, not part of the library).  A stored measurement is valid for this
-    hash only."""
+def code_only(src: str) -> str:
+    """C++ source without its comments, whitespace runs collapsed to one
+    space; string and character literals are kept as they are."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            while i < n and src[i] != "\n":
+                i += 1
+        elif src.startswith("/*", i):
+            k = src.find("*/", i + 2)
+            i = n if k < 0 else k + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
+def kernel_source_hash(read=None) -> str:
+    """Hash of the code (comments and layout aside) of every source that goes
+    into the library's kernels: all of csrc but the host-only ABI layer
+    (api.hip, no device code) and the probes (tools, not part of the
+    library).  A stored measurement is valid for this hash only.  `read`
+    (name -> text) replaces the working tree, e.g. to hash another revision."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "decode_kv_cache_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    if read is None:
+        names = os.listdir(csrc)
+
+        def read(f):
+            with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+                return fh.read()
+    else:
+        names = read(None)
+    for f in sorted(names):
         if f in ("probes.hip", "api.hip"):
             continue
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        h.update(f.encode() + b"\0" + code_only(read(f)).encode())
     return h.hexdigest()[:16]
 
 

@@ -83,3 +83,23 @@ def test_binding_rejects_host_tensors():
     kept = torch.zeros((s.num_seqs, s.num_layers, s.num_kv_heads, s.budget), dtype=torch.int32)
     with pytest.raises(ValueError, match="device"):
         K.kara_select_chunks(cfg, scores, kept)
+
+
+def test_kernel_hash_sees_code_not_comments():
+    """Stored traffic measurements stay valid across comment edits and go
+    stale on any code edit; the host-only ABI layer and the probes do not
+    count."""
+    from decode_kv_cache_amd.profiling import code_only, kernel_source_hash
+
+    base = {"a.hip": 'int f() { return 1; } // one\n', "b.h": "/* x */ #define S \"// kept\"\n",
+            "api.hip": "int g();", "probes.hip": "int p();"}
+
+    def reader(files):
+        return lambda f: list(files) if f is None else files[f]
+
+    h0 = kernel_source_hash(reader(base))
+    assert kernel_source_hash(reader(dict(base, **{"a.hip": "int f() {\n  return 1;  /* same */ }\n"}))) == h0
+    assert kernel_source_hash(reader(dict(base, **{"api.hip": "int g(int);", "probes.hip": ""}))) == h0
+    assert kernel_source_hash(reader(dict(base, **{"a.hip": "int f() { return 2; }"}))) != h0
+    assert kernel_source_hash(reader(dict(base, **{"b.h": '#define S "// changed"'}))) != h0
+    assert code_only('x = "a//b"; // c\ny') == 'x = "a//b"; y'
