@@ -1,5 +1,5 @@
 // Compaction kernels: one workgroup per unit copies the kept K and V rows
-// into place (compact_core.h), then one thread per sequence rewrites its
+// into place (compact_core.h), then one wave per sequence rewrites its
 // block table.  Kara's English abstract: the method is adapted to
 // PagedAttention and lowers KV-cache memory.
 #include "compact_core.h"
@@ -28,14 +28,16 @@ __global__ __launch_bounds__(CMP_THREADS) void compact_kernel(Geo g, unsigned ch
                                                    L, kept + unit * g.B, esize, tail_of(g, tails, n, L));
 }
 
-// One thread per sequence: freed list, table truncation, new length.
-__global__ void finalize_kernel(Geo g, int32_t* __restrict__ tables, const int32_t* __restrict__ prior,
-                                int32_t* __restrict__ seq_lens, int32_t* __restrict__ freed,
-                                int32_t* __restrict__ num_freed, int max_freed,
-                                const int32_t* __restrict__ tails) {
-  const int n = blockIdx.x * blockDim.x + threadIdx.x;
-  if (n >= g.S) return;
-  finalize_sequence(g, n, tables, prior, seq_lens, freed, num_freed, max_freed, tails);
+// One wave per sequence: freed list, table truncation, new length.
+constexpr int FIN_THREADS = 64;
+__global__ __launch_bounds__(FIN_THREADS) void finalize_kernel(Geo g, int32_t* __restrict__ tables,
+                                                               const int32_t* __restrict__ prior,
+                                                               int32_t* __restrict__ seq_lens,
+                                                               int32_t* __restrict__ freed,
+                                                               int32_t* __restrict__ num_freed, int max_freed,
+                                                               const int32_t* __restrict__ tails) {
+  finalize_sequence(g, blockIdx.x, tables, prior, seq_lens, freed, num_freed, max_freed, tails, threadIdx.x,
+                    FIN_THREADS);
 }
 
 hipError_t launch_compact(const Geo& g, int dtype, void* kc, void* vc, int32_t* tables, const int32_t* prior,
@@ -57,8 +59,9 @@ hipError_t launch_compact(const Geo& g, int dtype, void* kc, void* vc, int32_t* 
       hipLaunchKernelGGL(compact_kernel<512>, grid, dim3(CMP_THREADS), 0, st, g, (unsigned char*)kc,
                          (unsigned char*)vc, tables, prior, kept, tails, esize);
   }
-  hipLaunchKernelGGL(finalize_kernel, dim3((g.S + 255) / 256), dim3(256), 0, st, g, tables, prior, seq_lens,
-                     freed, num_freed, max_freed, tails);
+  if (g.S > 0)
+    hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)g.S), dim3(FIN_THREADS), 0, st, g, tables, prior, seq_lens,
+                       freed, num_freed, max_freed, tails);
   return hipGetLastError();
 }
 

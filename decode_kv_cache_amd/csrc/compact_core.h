@@ -85,11 +85,14 @@ __device__ inline int tail_of(const Geo& g, const int32_t* __restrict__ tails, i
   return (int)max(0LL, min((long long)tails[n], room));
 }
 
-// Freed list, table truncation and new length of sequence n (one thread).
+// Freed list, table truncation and new length of sequence n, by `nthreads`
+// threads of one workgroup (thread `tid`); freed entry k is table entry
+// nb_new + k, so the list stays in ascending logical order whatever the
+// thread count.
 __device__ inline void finalize_sequence(const Geo& g, int n, int32_t* __restrict__ tables,
                                          const int32_t* __restrict__ prior, int32_t* __restrict__ seq_lens,
                                          int32_t* __restrict__ freed, int32_t* __restrict__ num_freed,
-                                         int max_freed, const int32_t* __restrict__ tails = nullptr) {
+                                         int max_freed, const int32_t* __restrict__ tails, int tid, int nthreads) {
   const int L = prior[n];
   int32_t* row = tables + (long long)n * g.max_blocks;
   int32_t* fr = freed + (long long)n * max_freed;
@@ -99,16 +102,17 @@ __device__ inline void finalize_sequence(const Geo& g, int n, int32_t* __restric
     const long long nb_old_ll = ((long long)L + g.W + T + g.bs - 1) >> g.bs_shift;
     const int nb_old = (int)min(nb_old_ll, (long long)g.max_blocks);
     const int nb_new = (int)min((((long long)L + g.B + T + g.bs - 1) >> g.bs_shift), (long long)nb_old);
-    for (int b = nb_new; b < nb_old && cnt < max_freed; ++b) {
-      fr[cnt++] = row[b];
-      row[b] = -1;
+    cnt = min(nb_old - nb_new, max_freed);
+    for (int k = tid; k < cnt; k += nthreads) {
+      fr[k] = row[nb_new + k];
+      row[nb_new + k] = -1;
     }
-    seq_lens[n] = L + g.B + T;
-  } else {
+    if (tid == 0) seq_lens[n] = L + g.B + T;
+  } else if (tid == 0) {
     seq_lens[n] = L;
   }
-  num_freed[n] = cnt;
-  for (int k = cnt; k < max_freed; ++k) fr[k] = -1;
+  if (tid == 0) num_freed[n] = cnt;
+  for (int k = cnt + tid; k < max_freed; k += nthreads) fr[k] = -1;
 }
 
 }  // namespace kara

@@ -352,10 +352,10 @@ __global__ __launch_bounds__(FTHREADS, 1) void pipeline_kernel(Geo g, const __bf
     last = atomicAdd(&done[n], 1) == g.Lyr * g.Hkv - 1;
   }
   __syncthreads();
-  if (last && tid == 0) {
+  if (last) {                                       // the whole workgroup rewrites the table
     __threadfence();
-    finalize_sequence(g, n, tables, prior, seq_lens, freed, num_freed, max_freed);
-    done[n] = 0;
+    finalize_sequence(g, n, tables, prior, seq_lens, freed, num_freed, max_freed, nullptr, tid, FTHREADS);
+    if (tid == 0) done[n] = 0;
   }
 }
 
