@@ -65,6 +65,11 @@ SMALL = [
               window=255, budget=51, seeds=3, radius=3, prior=("uniform", 1, 99), key_model="outliers"),
     KaraShape("f32_d64_w300_two_pass", 121, num_seqs=2, num_layers=1, num_q_heads=4, num_kv_heads=2, head_dim=64,
               window=300, budget=60, seeds=3, radius=4, prior=("uniform", 0, 64), dtype="f32", block_size=8),
+    # the largest query-row counts of the single-pass scorers: G = 16 over their longest windows
+    KaraShape("f32_d64_w256_g16", 122, num_seqs=1, num_layers=1, num_q_heads=16, num_kv_heads=1, head_dim=64,
+              window=256, budget=64, seeds=4, radius=3, prior=("fixed", 5), dtype="f32", plants=True),
+    KaraShape("bf16_w1024_g16", 123, num_seqs=1, num_layers=1, num_q_heads=32, num_kv_heads=2, head_dim=128,
+              window=1024, budget=204, seeds=8, radius=5, prior=("fixed", 77), key_model="outliers"),
 ]
 
 
