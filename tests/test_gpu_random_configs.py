@@ -68,11 +68,20 @@ def test_random_configuration(i):
         assert freed[n, :int(ref["num_freed"][n])].tolist() == ref["freed"][n].tolist()
 
 
-@pytest.mark.parametrize("i", range(24))
+def _one_launch_cases():
+    """Indices of the configurations where kara_compress_fused is offered (a
+    single-pass scorer runs); the library answers on the host."""
+    from decode_kv_cache_amd import kara as K
+    return [i for i in range(24)
+            if K.kara_compress_fused_supported(K.make_config(_random_shape(i)[0], max_blocks_per_seq=4096,
+                                                             num_blocks=100000))]
+
+
+@pytest.mark.parametrize("i", _one_launch_cases())
 def test_random_configuration_one_launch(i):
     """The same configurations through kara_compress_fused, where it is
-    offered (a single-pass scorer runs): every output, pool byte and table
-    equal to the three calls' bit for bit (reading R29)."""
+    offered: every output, pool byte and table equal to the three calls' bit
+    for bit (reading R29)."""
     import torch
 
     from decode_kv_cache_amd import kara as K
@@ -80,8 +89,7 @@ def test_random_configuration_one_launch(i):
     s, _ = _random_shape(i)
     wa = make_workload(s, "cuda")
     cfg = config_of(wa)
-    if not K.kara_compress_fused_supported(cfg):
-        pytest.skip("two-pass scorer shape: the one-launch pipeline is not offered")
+    assert K.kara_compress_fused_supported(cfg)
     wb = make_workload(s, "cuda")
     _, ref = run_step(wa, cfg)
     out = Outputs(cfg, "cuda")
