@@ -35,7 +35,7 @@ template <int NT>
 struct SelScratch {
   int hist[256];
   int wave_tot[NT / 64];
-  int bcast[2];
+  int bcast[3];
 };
 
 // Exclusive prefix sum of v over the block in thread order; *total gets the sum.
@@ -63,8 +63,11 @@ __device__ inline int block_scan(int v, int* total, SelScratch<NT>& sh) {
 }
 
 // Find the k-th largest key (1-based) among positions whose flag has
-// (flag & emask) == 0.  Returns the key value T; *need = how many of the
-// eligible positions equal to T belong to the top k (lowest positions first).
+// (flag & emask) == 0.  Returns a threshold T and *need such that the top k
+// are exactly the eligible keys > T plus the first *need eligible keys equal
+// to T (lowest positions first).  When a digit's bucket holds exactly the k
+// keys still wanted, every key with that prefix is taken and the search stops
+// early: T is then the largest key below the prefix and *need = 0.
 template <int NT>
 __device__ uint32_t radix_select(const uint32_t* keys, const uint8_t* flags, uint8_t emask, int W, int E, int k,
                                  int* need, SelScratch<NT>& sh) {
@@ -87,12 +90,18 @@ __device__ uint32_t radix_select(const uint32_t* keys, const uint8_t* flags, uin
     if (before < k && k <= before + c) {
       sh.bcast[0] = 255 - t;
       sh.bcast[1] = k - before;
+      sh.bcast[2] = c;
     }
     __syncthreads();
     prefix |= (uint32_t)sh.bcast[0] << shift;
     pmask |= 0xFFu << shift;
     k = sh.bcast[1];
+    const bool whole = k == sh.bcast[2] && prefix != 0u;   // the same in every thread
     __syncthreads();
+    if (whole && shift > 0) {
+      *need = 0;
+      return prefix - 1u;                         // every key >= prefix, nothing below it
+    }
   }
   *need = k;
   return prefix;
