@@ -135,8 +135,10 @@ def test_empty_batch_is_a_no_op():
     assert out.guards_intact()
 
 
-def test_repeat_runs_are_bit_identical_and_stream_ordered():
-    s = SMALL[1]
+@pytest.mark.parametrize("idx", [1, 0, 12], ids=["resident_keys", "staged_keys", "two_pass"])
+def test_repeat_runs_are_bit_identical_and_stream_ordered(idx):
+    """Every scorer reduces in a fixed order: two runs give the same bits."""
+    s = SMALL[idx]
     res = []
     for _ in range(2):
         wl = make_workload(s, "cuda")
