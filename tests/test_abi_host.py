@@ -170,3 +170,28 @@ def test_allocation_free_pipeline_checks_before_device_work():
     assert L.kara_compress_fused_noalloc(ctypes.byref(_cfg(num_seqs=65537, num_layers=1)), *args) == -6
     assert L.kara_compress_fused_noalloc(ctypes.byref(_cfg(num_seqs=0)), *args) == 0
     assert "scratch" in K.kara_status_str(-6)
+
+
+def test_workspace_grows_with_the_shape():
+    """The two-pass scorer's workspace never shrinks when the batch, the
+    layers, the heads or the window grow (and is 0 wherever a single-pass
+    scorer runs)."""
+    base = dict(window=1500, budget=300, seeds=6, radius=4, head_dim=64)
+    prev = None
+    for S in (1, 2, 7, 64):
+        w = K.kara_workspace_bytes(_cfg(num_seqs=S, **base))
+        assert prev is None or w >= prev
+        prev = w
+    for field, values in (("num_layers", (1, 2, 32)), ("window", (1500, 2048, 4096, 8192))):
+        prev = None
+        for v in values:
+            w = K.kara_workspace_bytes(_cfg(**dict(base, **{field: v})))
+            assert w > 0 and (prev is None or w >= prev), (field, v)
+            prev = w
+    prev = None
+    for G in (1, 2, 4, 8):
+        w = K.kara_workspace_bytes(_cfg(num_q_heads=8 * G, num_kv_heads=8, **base))
+        assert prev is None or w >= prev
+        prev = w
+    for W in (16, 128, 256):
+        assert K.kara_workspace_bytes(_cfg(head_dim=64, window=W, budget=W // 2, seeds=1, radius=1)) == 0
