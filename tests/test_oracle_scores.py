@@ -136,3 +136,26 @@ def test_huge_logits_stay_finite():
     c = window_scores(q, k)
     assert np.all(np.isfinite(c))
     assert abs(c.sum() - 60) < 1e-9
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_scalar_loops_on_tiny_inputs(seed):
+    """Scalar loops with math.exp on tiny inputs (W <= 16, d <= 8, G <= 3):
+    the softmax of every query row over the window keys, summed down each
+    column, element by element, with no array arithmetic.  The closed forms
+    above are the pins; this cross-checks the array code's indexing."""
+    rng = np.random.default_rng(900 + seed)
+    G, W, d = int(rng.integers(1, 4)), int(rng.integers(1, 17)), int(rng.integers(1, 9))
+    q = rng.normal(size=(G, W, d)) * float(rng.choice([0.3, 1.0, 3.0]))
+    k = rng.normal(size=(W, d))
+    want = [0.0] * W
+    for h in range(G):
+        for i in range(W):
+            logits = [sum(float(q[h, i, e]) * float(k[j, e]) for e in range(d)) / math.sqrt(d) for j in range(W)]
+            top = max(logits)
+            ex = [math.exp(x - top) for x in logits]
+            tot = sum(ex)
+            for j in range(W):
+                want[j] += ex[j] / tot
+    got = window_scores(q, k)
+    assert np.allclose(got, np.array(want), rtol=1e-12, atol=0)
