@@ -102,3 +102,50 @@ def test_noalloc_replayed_from_a_captured_graph():
         res = {k: bits(out[k]) for k in ("scores", "kept", "mask", "seq_lens", "freed", "num_freed")}
         res.update(k=bits(wl.k_pool), v=bits(wl.v_pool), tables=wl.block_tables.cpu().numpy())
         _same(ref, res, f"replay {i}")
+
+
+
+def _flat_run(S, noalloc, seed=4242, W=32, B=8, bs=16, d=64):
+    """S one-layer, one-head bf16 sequences with prior length 0, random
+    queries and pools, block tables a seeded permutation of the pool; one
+    call of either entry point."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    per = -(-W // bs)
+    nb = S * per
+    q = torch.randn((S, 1, W, 1, d), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn((1, nb, 1, bs, d), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((1, nb, 1, bs, d), generator=g, device="cuda").to(torch.bfloat16)
+    tables = torch.randperm(nb, generator=g, device="cuda").to(torch.int32).view(S, per).contiguous()
+    prior = torch.zeros(S, dtype=torch.int32, device="cuda")
+    cfg = K.kara_config(S, 1, 1, 1, d, W, B, 1, 1, bs, K.KARA_BF16, per, nb)
+    assert K.kara_check_config(cfg) == 0 and K.kara_compress_fused_supported(cfg)
+    out = Outputs(cfg, "cuda")
+    args = (cfg, q, k, v, tables, prior, out["scores"], out["kept"], out["seq_lens"], out["freed"], out["num_freed"])
+    torch.cuda.synchronize()
+    if noalloc:
+        K.kara_compress_fused_noalloc(*args, mask=out["mask"])
+    else:
+        done = torch.zeros(S, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        K.kara_compress_fused(*args, done, mask=out["mask"])
+    torch.cuda.synchronize()
+    assert out.guards_intact()
+    res = {key: bits(out[key]) for key in ("scores", "kept", "mask", "seq_lens", "freed", "num_freed")}
+    res.update(k=bits(k), v=bits(v), tables=tables.cpu().numpy())
+    if not noalloc:
+        assert bool((done == 0).all())
+    return res
+
+
+def test_noalloc_at_the_scratch_limit():
+    """Exactly KARA_NOALLOC_MAX_SEQS = 65536 sequences, then 3, then 65536
+    again: each allocation-free call equals kara_compress_fused bit for bit,
+    so every counter of the fixed array was used and returned to zero."""
+    print("[noalloc] 65536 sequences, then 3, then 65536", flush=True)
+    S = 65536
+    ref = _flat_run(S, False)
+    assert (ref["seq_lens"] == 8).all() and (ref["num_freed"] == 1).all()
+    _same(ref, _flat_run(S, True), "65536 sequences")
+    _same(_flat_run(3, False, seed=7), _flat_run(3, True, seed=7), "3 sequences")
+    _same(ref, _flat_run(S, True), "65536 sequences again")
