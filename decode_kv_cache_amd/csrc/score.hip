@@ -154,11 +154,16 @@ __global__ __launch_bounds__(256) void row_lse_kernel(Geo g, const T* __restrict
     lds_half_row<T, D>(lds[buf], col, half, ak);
     acc[0] = f32x16{};
     acc[1] = f32x16{};
+    // raised issue priority while the MFMAs issue: of the waves sharing a
+    // SIMD (several workgroups per compute unit), one with MFMAs ready goes
+    // first while the others run their exponentials
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       acc[0] = M::mma(ak[f], bq[0][f], acc[0]);
       acc[1] = M::mma(ak[f], bq[1][f], acc[1]);
     }
+    __builtin_amdgcn_s_setprio(0);
     // acc[s][r]: key kt*32 + 8*(r/4) + 4*half + (r%4) against query row row0 + 32 s + col
   };
   for (int kt = 0; kt < full; ++kt) {
@@ -314,11 +319,13 @@ __global__ __launch_bounds__(256) void col_mass_kernel(Geo g, const T* __restric
     typename M::frag aq[NF];
     lds_half_row<T, D>(lds[buf], col, half, aq);
     f32x16 acc[2] = {{}, {}};
+    __builtin_amdgcn_s_setprio(1);              // as in pass 1
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       acc[0] = M::mma(aq[f], bk[0][f], acc[0]);
       acc[1] = M::mma(aq[f], bk[1][f], acc[1]);
     }
+    __builtin_amdgcn_s_setprio(0);
     // acc[s][r]: query row rt*32 + 8*(r/4) + 4*half + (r%4) against key key0 + 32 s + col
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {

@@ -19,9 +19,11 @@
 //   - every logit's softmax weight is a per-lane scalar times its
 //     exponential, and the column sums accumulate lane-locally across all
 //     blocks of the unit; they are reduced over the 16 query lanes once, at
-//     the end.
+//     the end.  A block's column updates are issued among the next block's
+//     MFMAs, and so is most of the next block's row max.
 // Each logit is computed once and exponentiated once.
 #include <mutex>
+#include <type_traits>
 
 #include "compact_core.h"
 #include "kara_device.h"
@@ -63,6 +65,21 @@ __device__ __forceinline__ float group_sum(float v) {
   v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// max over the 8 logits of two tiles, starting from m (or from the first
+// logit when FIRST): three-input maxima, two new logits per instruction
+__device__ __forceinline__ float pair_max(bool first, float m, const f32x4v& a, const f32x4v& b) {
+  if (first) {
+    m = fmaxf(fmaxf(a[0], a[1]), a[2]);
+    m = fmaxf(fmaxf(m, a[3]), b[0]);
+    m = fmaxf(fmaxf(m, b[1]), b[2]);
+    return fmaxf(m, b[3]);
+  }
+  m = fmaxf(fmaxf(m, a[0]), a[1]);
+  m = fmaxf(fmaxf(m, a[2]), a[3]);
+  m = fmaxf(fmaxf(m, b[0]), b[1]);
+  return fmaxf(fmaxf(m, b[2]), b[3]);
 }
 
 // Per block, each wave exponentiates its logits against its own row maximum
@@ -117,9 +134,20 @@ __device__ __forceinline__ void fused_unit(const Geo& g, int unit, const __bf16*
   uint2 stage1 = q_fetch(min(1, nblk - 1));    // tile b+1
   __syncthreads();
   const float alpha = g.alpha;
-  // one block: consume tile b (in LDS), publish tile b+1 (held in `cur`) and
-  // start fetching tile b+2 into `nxt`
-  auto block = [&](int b, uint2& cur, uint2& nxt) {
+  // Each block is split in two steps.  logits(b) fetches tile b+2, reads tile
+  // b from LDS and computes the block's logits; when the previous block's
+  // exponentials are still in `acc` (PREV), each tile's four are folded into
+  // the column sums, with that block's weight, before the tile's accumulator
+  // takes the new logits, so the column updates of block b-1 issue among the
+  // MFMAs of block b.  stats(b) turns the logits into exponentials,
+  // publishes the wave's (max, sum) pair and tile b+1, and after the block's
+  // barrier combines the pairs into this wave's weight for block b.  Every
+  // column sum still takes its terms in block order, as one FMA each.
+  f32x4v acc[KTW];
+  float wgt = 0.f;
+  float pmx = 0.f;   // running row max over the tiles finished so far (no mask)
+  auto logits = [&](auto prev, int b, uint2& nxt) {
+    constexpr bool PREV = decltype(prev)::value;
     const int buf = b & 1;
     nxt = q_fetch(min(b + 2, nblk - 1));
     // B operand: query row qlane of this block, head_dim range [32 grp, 32 grp + 32)
@@ -132,15 +160,69 @@ __device__ __forceinline__ void fused_unit(const Geo& g, int unit, const __bf16*
         __builtin_memcpy(&qf[s], &v, 16);
       }
     }
-    // logits S^T: acc[t][r] = k[kbase + 16t + r] . q[row 16b + qlane]
-    // (reduction step outermost: 8 independent MFMAs between dependent ones)
-    f32x4v acc[KTW];
+    // logits S^T: acc[t][r] = k[kbase + 16t + r] . q[row 16b + qlane], two
+    // tiles at a time (each tile's four MFMAs chain on one accumulator).
+    // The previous block's column updates (32 FMAs) and the row max over the
+    // tiles already finished (12 three-input maxima) have no dependence on
+    // these MFMAs, so they are issued between them: the matrix core runs an
+    // MFMA for 16 cycles while the vector unit takes about two instructions.
+    // The section is fenced by scheduling barriers; empty asm statements pin
+    // its inputs (query fragments, previous exponentials) and outputs (logits,
+    // column sums) to it, and group barriers set the order MFMA, vector
+    // instruction(s), MFMA, ...  The wave raises its issue priority for the
+    // section so that, of the two waves sharing a SIMD, the one with MFMAs
+    // ready goes first.
+    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t = 0; t < KTW; ++t) acc[t] = mfma16(kf[t][0], qf[0], f32x4v{0.f, 0.f, 0.f, 0.f});
+    for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(qf[s]));
+    if (PREV) {
 #pragma unroll
-    for (int s = 1; s < 4; ++s)
+      for (int t = 0; t < KTW; ++t) asm volatile("" : "+v"(acc[t]));
+    }
 #pragma unroll
-      for (int t = 0; t < KTW; ++t) acc[t] = mfma16(kf[t][s], qf[s], acc[t]);
+    for (int t0 = 0; t0 < KTW; t0 += 2) {
+      f32x4v n0 = mfma16(kf[t0][0], qf[0], f32x4v{0.f, 0.f, 0.f, 0.f});
+      f32x4v n1 = mfma16(kf[t0 + 1][0], qf[0], f32x4v{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int s = 1; s < 4; ++s) {
+        n0 = mfma16(kf[t0][s], qf[s], n0);
+        n1 = mfma16(kf[t0 + 1][s], qf[s], n1);
+      }
+      if (PREV) {
+#pragma unroll
+        for (int t = t0; t < t0 + 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) colacc[t][r] = __builtin_fmaf(acc[t][r], wgt, colacc[t][r]);
+      }
+      // the previous pair's logits are complete: extend the row max over them
+      if (!MASK && t0 > 0) pmx = pair_max(t0 == 2, pmx, acc[t0 - 2], acc[t0 - 1]);
+      acc[t0] = n0;
+      acc[t0 + 1] = n1;
+    }
+#pragma unroll
+    for (int t = 0; t < KTW; ++t) asm volatile("" : "+v"(acc[t]));
+    if (PREV) {
+#pragma unroll
+      for (int t = 0; t < KTW; ++t) asm volatile("" : "+v"(colacc[t]));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 12; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, MASK ? 1 : 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  auto stats = [&](int b, uint2& cur) {
+    const int buf = b & 1;
     if (MASK) {                                  // keys past the window take no part
 #pragma unroll
       for (int t = 0; t < KTW; ++t)
@@ -150,11 +232,16 @@ __device__ __forceinline__ void fused_unit(const Geo& g, int unit, const __bf16*
     }
     // wave-local row max (raw logits)
     // (a linear chain of three-input maxima: two new logits per instruction)
-    float mx = fmaxf(fmaxf(acc[0][0], acc[0][1]), acc[0][2]);
-    mx = fmaxf(fmaxf(mx, acc[0][3]), acc[1][0]);
+    float mx;
+    if (MASK) {
+      mx = fmaxf(fmaxf(acc[0][0], acc[0][1]), acc[0][2]);
+      mx = fmaxf(fmaxf(mx, acc[0][3]), acc[1][0]);
 #pragma unroll
-    for (int i = 5; i + 1 < 4 * KTW; i += 2) mx = fmaxf(fmaxf(mx, acc[i >> 2][i & 3]), acc[(i + 1) >> 2][(i + 1) & 3]);
-    mx = fmaxf(mx, acc[KTW - 1][3]);
+      for (int i = 5; i + 1 < 4 * KTW; i += 2) mx = fmaxf(fmaxf(mx, acc[i >> 2][i & 3]), acc[(i + 1) >> 2][(i + 1) & 3]);
+      mx = fmaxf(mx, acc[KTW - 1][3]);
+    } else {
+      mx = pair_max(false, pmx, acc[KTW - 2], acc[KTW - 1]);
+    }
     mx = group_max(mx);
     const float ma = mx * alpha;                 // row max in base-2 exponent units
     const float moff = MASK && mx == -INFINITY ? 0.f : -ma;
@@ -188,17 +275,28 @@ __device__ __forceinline__ void fused_unit(const Geo& g, int unit, const __bf16*
     const float l = group_sum(pp.y * fast_exp2(pp.x - m) + pp.w * fast_exp2(pp.z - m));   // m_w = -inf -> 0
     // this wave's weight; rows past G*W contribute nothing
     const float own = MASK && mx == -INFINITY ? 0.f : fast_exp2(ma - m);
-    const float wgt = (LIN || b * QB + qlane < g.GW) ? own * __builtin_amdgcn_rcpf(l) : 0.f;
-#pragma unroll
-    for (int t = 0; t < KTW; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) colacc[t][r] = __builtin_fmaf(acc[t][r], wgt, colacc[t][r]);
+    wgt = (LIN || b * QB + qlane < g.GW) ? own * __builtin_amdgcn_rcpf(l) : 0.f;
   };
   uint2 stage2;
-  for (int b = 0; b < nblk; b += 2) {
-    block(b, stage1, stage2);
-    if (b + 1 < nblk) block(b + 1, stage2, stage1);
+  // even blocks fetch into stage2 and publish stage1, odd blocks the reverse;
+  // on entry to each pass of the loop `acc` holds the logits of block b
+  logits(std::false_type{}, 0, stage2);
+  int b = 0;
+  for (; b + 2 < nblk; b += 2) {
+    stats(b, stage1);
+    logits(std::true_type{}, b + 1, stage1);
+    stats(b + 1, stage2);
+    logits(std::true_type{}, b + 2, stage2);
   }
+  stats(b, stage1);
+  if (b + 1 < nblk) {
+    logits(std::true_type{}, b + 1, stage1);
+    stats(b + 1, stage2);
+  }
+#pragma unroll
+  for (int t = 0; t < KTW; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) colacc[t][r] = __builtin_fmaf(acc[t][r], wgt, colacc[t][r]);
   // column sums over the 16 query lanes of each lane group (xor within 16 lanes)
 #pragma unroll
   for (int t = 0; t < KTW; ++t)
