@@ -154,16 +154,11 @@ __global__ __launch_bounds__(256) void row_lse_kernel(Geo g, const T* __restrict
     lds_half_row<T, D>(lds[buf], col, half, ak);
     acc[0] = f32x16{};
     acc[1] = f32x16{};
-    // raised issue priority while the MFMAs issue: of the waves sharing a
-    // SIMD (several workgroups per compute unit), one with MFMAs ready goes
-    // first while the others run their exponentials
-    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       acc[0] = M::mma(ak[f], bq[0][f], acc[0]);
       acc[1] = M::mma(ak[f], bq[1][f], acc[1]);
     }
-    __builtin_amdgcn_s_setprio(0);
     // acc[s][r]: key kt*32 + 8*(r/4) + 4*half + (r%4) against query row row0 + 32 s + col
   };
   for (int kt = 0; kt < full; ++kt) {
@@ -319,7 +314,11 @@ __global__ __launch_bounds__(256) void col_mass_kernel(Geo g, const T* __restric
     typename M::frag aq[NF];
     lds_half_row<T, D>(lds[buf], col, half, aq);
     f32x16 acc[2] = {{}, {}};
-    __builtin_amdgcn_s_setprio(1);              // as in pass 1
+    // raised issue priority while the MFMAs issue: of the waves sharing a
+    // SIMD (three workgroups per compute unit), one with MFMAs ready goes
+    // first while the others run their exponentials.  (Pass 1 runs slower
+    // with it: its per-tile rescaling chain is what its waves wait on.)
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       acc[0] = M::mma(aq[f], bk[0][f], acc[0]);
