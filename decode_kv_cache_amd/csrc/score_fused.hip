@@ -293,6 +293,7 @@ __device__ __forceinline__ void fused_unit(const Geo& g, int unit, const __bf16*
     logits(std::true_type{}, b + 1, stage1);
     stats(b + 1, stage2);
   }
+  // the last block's exponentials, which no further MFMAs overwrite
 #pragma unroll
   for (int t = 0; t < KTW; ++t)
 #pragma unroll
