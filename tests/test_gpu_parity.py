@@ -70,6 +70,17 @@ SMALL = [
               window=256, budget=64, seeds=4, radius=3, prior=("fixed", 5), dtype="f32", plants=True),
     KaraShape("bf16_w1024_g16", 123, num_seqs=1, num_layers=1, num_q_heads=32, num_kv_heads=2, head_dim=128,
               window=1024, budget=204, seeds=8, radius=5, prior=("fixed", 77), key_model="outliers"),
+    # the resident-key scorer's block loop with one, two and three 16-row blocks (its loop is unrolled
+    # by two, with the first block and the last one or two outside it), and over a full window of
+    # 1024 keys with G = 3, whose blocks straddle window positions
+    KaraShape("fused_one_block", 124, num_seqs=2, num_layers=1, num_q_heads=1, num_kv_heads=1, head_dim=128,
+              window=16, budget=4, seeds=1, radius=1, prior=("fixed", 9)),
+    KaraShape("fused_two_blocks_g3", 125, num_seqs=1, num_layers=2, num_q_heads=3, num_kv_heads=1, head_dim=128,
+              window=7, budget=3, seeds=1, radius=1, prior=("uniform", 0, 20)),
+    KaraShape("fused_three_blocks", 126, num_seqs=1, num_layers=1, num_q_heads=2, num_kv_heads=2, head_dim=128,
+              window=48, budget=10, seeds=2, radius=2, prior=("fixed", 30), plants=True),
+    KaraShape("fused_w1024_g3", 127, num_seqs=1, num_layers=1, num_q_heads=6, num_kv_heads=2, head_dim=128,
+              window=1024, budget=204, seeds=8, radius=5, prior=("fixed", 5), key_model="student_t3", plants=True),
 ]
 
 

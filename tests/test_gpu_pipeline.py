@@ -27,6 +27,11 @@ SHAPES = [
               window=1024, budget=204, seeds=8, radius=5, prior=("uniform", 0, 3000), plants=True),
     KaraShape("pipe_w1_keepall", 305, num_seqs=2, num_layers=1, num_q_heads=2, num_kv_heads=1, head_dim=128,
               window=33, budget=33, seeds=1, radius=0, prior=("fixed", 3), block_size=8),
+    # one and three 16-row blocks per unit (the scorer's block loop runs zero and one times)
+    KaraShape("pipe_one_block", 310, num_seqs=3, num_layers=1, num_q_heads=2, num_kv_heads=2, head_dim=128,
+              window=16, budget=5, seeds=1, radius=2, prior=("uniform", 0, 40)),
+    KaraShape("pipe_three_blocks_g3", 311, num_seqs=2, num_layers=2, num_q_heads=3, num_kv_heads=1, head_dim=128,
+              window=16, budget=6, seeds=2, radius=1, prior=("fixed", 16), block_size=8),
     # windows of at most 256 keys outside bf16 / head_dim 128: the staged-key scorer
     shape_by_name("tiny"),
     KaraShape("pipe_f32_d64_g7_w256", 306, num_seqs=3, num_layers=2, num_q_heads=7, num_kv_heads=1, head_dim=64,
