@@ -130,13 +130,15 @@ __global__ __launch_bounds__(256) void row_lse_kernel(Geo g, const T* __restrict
         for (int r = 0; r < 16; ++r)
           if (kt * TILE + 8 * (r >> 2) + 4 * half + (r & 3) >= g.W) acc[s][r] = -INFINITY;
       }
-      float tmax = fmaxf(acc[s][0], acc[s][1]);
+      // a chain of three-input maxima: two new logits per instruction
+      float tmax = fmaxf(fmaxf(acc[s][0], acc[s][1]), acc[s][2]);
 #pragma unroll
-      for (int r = 2; r < 16; r += 2) tmax = fmaxf(tmax, fmaxf(acc[s][r], acc[s][r + 1]));
+      for (int r = 3; r + 1 < 16; r += 2) tmax = fmaxf(fmaxf(tmax, acc[s][r]), acc[s][r + 1]);
+      tmax = fmaxf(tmax, acc[s][15]);
       const float mnew = fmaxf(m[s], tmax * g.alpha);
-      float sum = 0.f;
+      float sum = fast_exp2(__builtin_fmaf(acc[s][0], g.alpha, -mnew));
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sum += fast_exp2(__builtin_fmaf(acc[s][r], g.alpha, -mnew));
+      for (int r = 1; r < 16; ++r) sum += fast_exp2(__builtin_fmaf(acc[s][r], g.alpha, -mnew));
       if (!partial || mnew != -INFINITY) {
         l[s] = l[s] * fast_exp2(m[s] - mnew) + sum;   // m = -inf -> factor 0
         m[s] = mnew;
